@@ -1,0 +1,309 @@
+"""Benchmark of the block-scaled GEMM hot path on one MI355X.
+
+Default workload (one "step" = one pass of the MoE expert forward hot path):
+  E = 32 experts, 16384 tokens x top-4 = 65536 routed rows; per-expert
+  counts ~ Multinomial(65536, Dirichlet(1)), each group padded to a multiple
+  of 128 rows (cumulative int32 ends); K = 4096, gate|up N = 2 x 1536.
+    1. hq_group_wise_quant     MXFP8 quantisation of the [R, 4096] activations
+    2. hq_group_contiguous_gemm  [R, 4096] x [32, 3072, 4096]^T -> BF16 [R, 3072]
+    3. hq_fused_swiglu_quant   y = up * silu(gate) on the valid rows -> MXFP8
+  Weights are quantised once before timing (they are static parameters).
+
+Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
+of the valid rows per second), the per-kernel times, the roofline of the
+dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
+and the oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload moe|dense_fp4|masked_fp4]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4_bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+METRIC = "MXFP8/MXFP4 grouped GEMM TFLOP/s + % MFMA peak; quant/SwiGLU GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _dev_bf16(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Timer:
+    """Per-kernel HIP-event timing on the stream the kernels run on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def mark(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.ev[name]]))
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch measured with counters (profiles/traffic.json),
+    or None when no measurement of the current kernel exists."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        return t.get(kernel_key)
+    except (OSError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- MoE workload
+def run_moe(args, torch, hq, synth):
+    dev = torch.device("cuda:0")
+    log("generating MoE inputs (E=32, 65536 routed rows, K=4096, N=3072)")
+    d = synth.moe_contiguous(threads=16)
+    counts, ends = d["counts"], d["group_end"]
+    R, K, N, H, E = int(ends[-1]), d["K"], d["N"], d["H"], len(counts)
+    T = int(counts.sum())
+    x = _dev_bf16(torch, d["a"], dev)
+    w_bf16 = _dev_bf16(torch, d["b"].reshape(E * N, K), dev)
+    wq, wsf, _ = hq.quantize(w_bf16, "mxfp8")
+    del w_bf16
+    wq = wq.view(E, N, K)
+    wsf = wsf.view(E, N, K // 32)
+    ge = torch.from_numpy(ends.astype(np.int32)).to(dev)
+    valid = torch.from_numpy(counts.astype(np.int32)).to(dev)
+    aq = torch.empty(R, K, dtype=torch.uint8, device=dev)
+    asf = torch.empty(R, K // 32, dtype=torch.uint8, device=dev)
+    out = torch.empty(R, N, dtype=torch.bfloat16, device=dev)
+    yq = torch.empty(R, H, dtype=torch.uint8, device=dev)
+    ysf = torch.empty(R, H // 32, dtype=torch.uint8, device=dev)
+
+    timer = Timer(torch)
+
+    def step(t=None):
+        f1 = lambda: hq.hq_group_wise_quant("mxfp8", x, aq, asf)
+        f2 = lambda: hq.hq_group_contiguous_gemm("mxfp8", aq, asf, wq, wsf, ge, out)
+        f3 = lambda: hq.hq_fused_swiglu_quant("mxfp8", out, yq, ysf, E, ge, 0, valid)
+        if t is None:
+            f1(); f2(); f3()
+        else:
+            t.mark("quant", f1)
+            t.mark("gemm", f2)
+            t.mark("swiglu", f3)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # separate pass with per-kernel events (same launches, same stream)
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+
+    ms_step = wall * 1e3 / args.steps
+    flops = 2.0 * T * N * K
+    quant_bytes = T * K * (2 + 1 + 1 / 32)
+    swiglu_bytes = T * H * (4 + 1 + 1 / 32)
+    gemm_ms = timer.mean_ms("gemm")
+    quant_ms = timer.mean_ms("quant")
+    sw_ms = timer.mean_ms("swiglu")
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    kernels = {
+        "quant_mxfp8": {"ms": quant_ms, "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9,
+                        "frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "grouped_gemm_mxfp8": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
+                               "frac_mfma": gemm_tflops / PEAK_TFLOPS["mxfp8"]},
+        "swiglu_quant_mxfp8": {"ms": sw_ms, "GB/s": swiglu_bytes / (sw_ms * 1e-3) / 1e9,
+                               "frac_hbm": swiglu_bytes / (sw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+    cfg = {"workload": "moe_grouped_contiguous_mxfp8_E32_T65536_K4096_N3072_swiglu",
+           "experts": E, "routed_rows": T, "padded_rows": R, "k": K, "n": N, "h": H,
+           "group_align": 128}
+    roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_TFLOPS["mxfp8"],
+            "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_TFLOPS["mxfp8"],
+            "traffic": _traffic("grouped_gemm_mxfp8"),
+            "kernel": "grouped_gemm_mxfp8", "flop_per_launch": flops}
+    value = flops / (ms_step * 1e-3) / 1e12
+    ctx = {"counts": counts, "ends": ends, "a": d["a"], "b": d["b"], "K": K, "N": N, "H": H}
+    return value, ms_step, cfg, roof, kernels, ctx
+
+
+def cpu_baseline_moe(ctx, budget_s=12.0):
+    """The oracle on a bounded sample of the same step: the first S routed rows
+    of expert 0 (quantise, GEMM against expert 0's weights, SwiGLU +
+    re-quantise).  Expert 0's weights are quantised by the oracle before the
+    clock starts, like the device path's static weights."""
+    from oracle import gemm as G
+    from oracle import quant as Q
+    from oracle import swiglu as S
+    K, N, H = ctx["K"], ctx["N"], ctx["H"]
+    w, wsf = Q.mx_quant_bf16(ctx["b"][0], "mxfp8")
+    rows = 8
+    spent = 0.0
+    while True:
+        xa = ctx["a"][:rows]
+        t0 = time.perf_counter()
+        a, sfa = Q.mx_quant_bf16(xa, "mxfp8")
+        out = G.dense_gemm("mxfp8", a, sfa, w, wsf)
+        S.swiglu_quant(out, H, "mxfp8")
+        spent = time.perf_counter() - t0
+        if spent > budget_s / 4 or rows >= int(ctx["counts"][0]):
+            break
+        rows = min(rows * 4, int(ctx["counts"][0]))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    tflops = 2.0 * rows * N * K / spent / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} routed rows of expert 0 (quant + GEMM vs expert 0 + SwiGLU/quant), "
+                      f"{spent:.2f} s"}
+
+
+# ---------------------------------------------------------------- other workloads
+def run_dense_fp4(args, torch, hq, synth):
+    dev = torch.device("cuda:0")
+    mode = args.mode
+    n, k, m = args.n, args.k, args.m
+    d = synth.dense_fp4_large(n, k, m)
+    x = _dev_bf16(torch, d["a"], dev)
+    w = _dev_bf16(torch, d["b"], dev)
+    wq, wsf, gw = hq.quantize(w, mode)
+    aq, asf, ga = hq.quantize(x, mode)
+    alpha = (ga * gw) if mode == "nvfp4" else None
+    out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+    f = lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        timer.mark("gemm", f)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("gemm")
+    flops = 2.0 * m * n * k
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["nvfp4_bf16" if mode == "nvfp4" else mode]
+    gs = 16 if mode == "nvfp4" else 32
+    bytes_ = (m + n) * k * (0.5 + 1 / gs) + 2 * m * n
+    cfg = {"workload": f"dense_{mode}_M{m}_N{n}_K{k}", "m": m, "n": n, "k": k}
+    roof = {"bound": "mfma" if m >= 512 else "hbm", "achieved": tf if m >= 512 else bytes_ / (ms * 1e-3) / 1e9,
+            "peak": peak if m >= 512 else PEAK_HBM_GBS, "unit": "TFLOP/s" if m >= 512 else "GB/s",
+            "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return tf, ms, cfg, roof, {"dense_gemm": {"ms": ms, "TFLOP/s": tf, "GB/s": bytes_ / (ms * 1e-3) / 1e9}}, None
+
+
+def run_masked_fp4(args, torch, hq, synth):
+    dev = torch.device("cuda:0")
+    d = synth.moe_masked(threads=16)
+    E, Mmax, K, N = 64, d["max_m"], d["K"], d["N"]
+    counts = d["counts"]
+    T = int(counts.sum())
+    x = _dev_bf16(torch, d["a"], dev)
+    aq, asf, _ = hq.quantize(x, "mxfp4")
+    w = _dev_bf16(torch, d["b"].reshape(E * N, K), dev)
+    wq, wsf, _ = hq.quantize(w, "mxfp4")
+    del w
+    wq, wsf = wq.view(E, N, K // 2), wsf.view(E, N, K // 32)
+    cnt = torch.from_numpy(counts.astype(np.int32)).to(dev)
+    out = torch.empty(E * Mmax, N, dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+    f = lambda: hq.hq_group_masked_gemm("mxfp4", aq, asf, wq, wsf, cnt, out, Mmax)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        timer.mark("gemm", f)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("gemm")
+    flops = 2.0 * T * N * K
+    experts = int((counts > 0).sum())
+    bytes_ = T * K * (0.5 + 1 / 32) + experts * N * K * (0.5 + 1 / 32) + 2 * T * N
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    cfg = {"workload": "moe_grouped_masked_mxfp4_E64_Mmax256_K7168_N4096", "routed_rows": T}
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    tf = flops / (ms * 1e-3) / 1e12
+    return tf, ms, cfg, roof, {"masked_gemm_mxfp4": {"ms": ms, "TFLOP/s": tf, "GB/s": gbs}}, None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4"])
+    ap.add_argument("--mode", default="mxfp4")
+    ap.add_argument("--m", type=int, default=4096)
+    ap.add_argument("--n", type=int, default=17408)
+    ap.add_argument("--k", type=int, default=5120)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_gemm_moe_amd as hq
+    import synth
+    hq.load()
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4}[args.workload]
+    value, ms_step, cfg, roof, kernels, ctx = runner(args, torch, hq, synth)
+    cpu = None
+    if ctx is not None and not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample (cpu_baseline)")
+        cpu = cpu_baseline_moe(ctx)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8" if args.workload == "moe" else args.mode,
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+"""Python binding of libhq.so, the MI355X (gfx950) block-scaled GEMM library.
+
+The functions carry the names of the C ABI (include/hq.h) and only marshal
+arguments: they check that the torch tensors have the dtypes, sizes, device
+and contiguity the C call assumes (the C layer cannot see buffer sizes), pass
+raw device pointers and the current HIP stream, and raise HQError on a
+non-zero status.  Every step of the computation runs in the HIP kernels;
+there is no CPU fallback.  If libhq.so has not been built, loading fails
+loudly (build it with ``python -m fp4_gemm_moe_amd.build``).
+
+PyTorch is used for device memory and streams only.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQError",
+    "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
+    "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
+    "hq_last_error", "library_path", "load", "EXPORTED_SYMBOLS",
+    "quantize", "group_size", "code_cols",
+]
+
+HQ_MXFP8 = 0
+HQ_MXFP4 = 1
+HQ_NVFP4 = 2
+HQ_GS_INPUT = 1
+
+MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
+         "w8a8-mxfp8": HQ_MXFP8, "w4a4-mxfp4": HQ_MXFP4, "w4a4-nvfp4": HQ_NVFP4}
+
+EXPORTED_SYMBOLS = (
+    "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
+    "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class HQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"hq status {status}: {msg}")
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "libhq.so")
+
+
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+
+_SIGS = {
+    "hq_last_error": ([], ctypes.c_char_p),
+    "hq_group_wise_quant": ([_VP, _I32, _VP, _I64, _I64, _VP, _VP, _VP, _U32], _I32),
+    "hq_dense_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
+    "hq_batch_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32], _I32),
+    "hq_group_contiguous_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
+                                  _I64, _I64, _I64, _I32], _I32),
+    "hq_group_masked_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _VP, _VP, _VP,
+                              _I64, _I64, _I32], _I32),
+    "hq_fused_swiglu_quant": ([_VP, _I32, _VP, _I64, _I64, _I32, _VP, _I64, _VP, _VP, _VP,
+                               _VP, _VP], _I32),
+}
+
+
+def load():
+    """Loads libhq.so once and declares the C signatures."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: the HIP library has not been built "
+                               "(python -m fp4_gemm_moe_amd.build)")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def hq_last_error():
+    return load().hq_last_error().decode()
+
+
+def _mode(mode):
+    if isinstance(mode, str):
+        return MODES[mode]
+    return int(mode)
+
+
+def group_size(mode):
+    return 16 if _mode(mode) == HQ_NVFP4 else 32
+
+
+def code_cols(mode, k):
+    """Bytes per row of the code tensor for logical width k."""
+    return k if _mode(mode) == HQ_MXFP8 else k // 2
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(*ts):
+    dev = next((t.device for t in ts if t is not None), None)
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, numel=None, shape_last=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _check(status):
+    if status != 0:
+        raise HQError(status, hq_last_error())
+
+
+# ---------------------------------------------------------------- the six calls
+def hq_group_wise_quant(mode, x, q, sf, global_scale=None, flags=0):
+    """x [m, k] bf16 -> q [m, K'] uint8, sf [m, k/gs] uint8 (in place).
+    NVFP4: global_scale is a float32 [1] tensor (read with HQ_GS_INPUT, else
+    written)."""
+    mode = _mode(mode)
+    m, k = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(q, "q", torch.uint8, m * code_cols(mode, k))
+    _need(sf, "sf", torch.uint8, m * (k // group_size(mode)))
+    _need(global_scale, "global_scale", torch.float32, 1)
+    _check(load().hq_group_wise_quant(_stream(x), mode, _p(x), m, k, _p(q), _p(sf),
+                                      _p(global_scale), flags))
+
+
+def _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, groups, bias_groups):
+    _need(a, "a", torch.uint8, rows * code_cols(mode, k))
+    _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
+    _need(b, "b", torch.uint8, groups * n * code_cols(mode, k))
+    _need(sfb, "sfb", torch.uint8, groups * n * (k // group_size(mode)))
+    _need(out, "out", torch.bfloat16, rows * n)
+    _need(bias, "bias", torch.bfloat16, bias_groups * n)
+    _need(alpha, "alpha", torch.float32, bias_groups)
+
+
+def hq_dense_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, m=None, n=None, k=None,
+                  cu_limit=0):
+    """out[m, n] = a[m, k] * b[n, k]^T (+bias[n]) (*alpha[0]) in BF16."""
+    mode = _mode(mode)
+    m = out.shape[0] if m is None else m
+    n = out.shape[-1] if n is None else n
+    k = a.shape[-1] * (1 if mode == HQ_MXFP8 else 2) if k is None else k
+    _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, m, n, k, 1, 1)
+    _check(load().hq_dense_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
+                                _p(alpha), _p(out), m, n, k, cu_limit))
+
+
+def hq_batch_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0):
+    """out[B, m, n] = a[B, m, k] * b[B, n, k]^T per batch item."""
+    mode = _mode(mode)
+    B, m, kc = a.shape
+    n = b.shape[1]
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, B * m, n, k, B, B)
+    _check(load().hq_batch_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
+                                _p(alpha), _p(out), B, m, n, k, cu_limit))
+
+
+def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, alpha=None,
+                             cu_limit=0):
+    """Group g (rows [group_end[g-1], group_end[g]) of a) times b[g]^T."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    E, n, _ = b.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    _need(group_end, "group_end", torch.int32, E)
+    _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, E, E)
+    _check(load().hq_group_contiguous_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
+                                           _p(group_end), E, _p(bias), _p(alpha), _p(out),
+                                           rows, n, k, cu_limit))
+
+
+def hq_group_masked_gemm(mode, a, sfa, b, sfb, masked_m, out, max_m, bias=None, alpha=None,
+                         cu_limit=0):
+    """Expert e: the first masked_m[e] rows of slot [e*max_m, (e+1)*max_m)."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    E, n, _ = b.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    if rows != E * max_m:
+        raise ValueError(f"a has {rows} rows, expected num_groups * max_m = {E * max_m}")
+    _need(masked_m, "masked_m", torch.int32, E)
+    _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, E, E)
+    _check(load().hq_group_masked_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
+                                       _p(masked_m), E, max_m, _p(bias), _p(alpha), _p(out),
+                                       n, k, cu_limit))
+
+
+def hq_fused_swiglu_quant(mode, x, q, sf, num_groups, group_end=None, slot_rows=0, valid=None,
+                          global_scale=None, y_debug=None):
+    """x [rows, 2h] = [gate | up] -> y = up * silu(gate) quantised into q, sf."""
+    mode = _mode(mode)
+    rows, h2 = x.shape
+    h = h2 // 2
+    _need(x, "x", torch.bfloat16)
+    _need(q, "q", torch.uint8, rows * code_cols(mode, h))
+    _need(sf, "sf", torch.uint8, rows * (h // group_size(mode)))
+    _need(group_end, "group_end", torch.int32, num_groups)
+    _need(valid, "valid", torch.int32, num_groups)
+    _need(global_scale, "global_scale", torch.float32, 1)
+    _need(y_debug, "y_debug", torch.float32, rows * h)
+    _check(load().hq_fused_swiglu_quant(_stream(x), mode, _p(x), rows, h, num_groups,
+                                        _p(group_end), slot_rows, _p(valid), _p(q), _p(sf),
+                                        _p(global_scale), _p(y_debug)))
+
+
+# ---------------------------------------------------------------- allocation helper
+def quantize(x, mode, global_scale=None):
+    """Allocates (q, sf, g) with torch and runs hq_group_wise_quant.  For
+    NVFP4, g is computed unless a float32 [1] global_scale is supplied."""
+    mode = _mode(mode)
+    m, k = x.shape
+    q = torch.empty((m, code_cols(mode, k)), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((m, k // group_size(mode)), dtype=torch.uint8, device=x.device)
+    g = None
+    flags = 0
+    if mode == HQ_NVFP4:
+        if global_scale is not None:
+            g = global_scale
+            flags = HQ_GS_INPUT
+        else:
+            g = torch.empty(1, dtype=torch.float32, device=x.device)
+    hq_group_wise_quant(mode, x, q, sf, g, flags)
+    return q, sf, g

@@ -1,0 +1,115 @@
+// Pieces shared by the GEMM kernels: the scaled-MFMA wrapper, the tile space
+// of a grouped problem, and the BF16 epilogue store.
+//
+// GEMM definition: HALOps "GEMM" page, dense_gemm section (output = input @
+// weight^T + bias, BF16 output); the grouped forms follow the batch_gemm,
+// group_contiguous_gemm and group_masked_gemm sections and cuDNN FE "Grouped
+// GEMM + dGLU (SM100)" Step 1 (sum over k of dequantize(A) * dequantize(B)).
+//
+// Matrix-core contract used here (gfx950 V_MFMA_SCALE_F32_16X16X128_F8F6F4):
+// operand src0 is a 16 x 128 tile, src1 a 128 x 16 tile; lane l supplies row
+// (l % 16) of src0 / column (l % 16) of src1, and lane group q = l / 16
+// supplies the E8M0 scale of K block [32q, 32q + 32) of that row.  Which
+// elements a lane's data registers hold depends on the element width (all
+// established on the device with integer-coded and one-hot probes):
+//   FP4 (4 dwords): elements [32q, 32q + 32), two per byte, low nibble first;
+//   FP8 (8 dwords): elements [16q, 16q + 16) in dwords 0-3 and
+//                   [64 + 16q, 64 + 16q + 16) in dwords 4-7.
+// The 16 x 16 FP32 result lands as D[4 * (l / 16) + r][l % 16] in
+// accumulator register r.  We feed the
+// weights as src0 and the activations as src1, so lane l holds
+// out[m = l % 16][n = 4 * (l / 16) + r]: four consecutive output columns,
+// one 8-byte BF16 store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fmt.hpp"
+#include "hq_internal.hpp"
+#include "sched.hpp"
+
+namespace hq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// FMT: 0 = FP8 E4M3 operands, 4 = FP4 E2M1 operands (the instruction's
+// cbsz / blgp format codes).
+template <int FMT>
+__device__ __forceinline__ v4f mfma_scaled(v8i w, v8i x, v4f acc, int sw, int sx) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, FMT, FMT, 0, sw, 0, sx);
+}
+
+// Rows owned by group g and the tile space (group m-tiles x n-tiles).
+struct GroupRows {
+  int64_t start;
+  int64_t count;
+};
+
+// LDS tables for grouped forms: per group start row, row count and the
+// inclusive prefix of m-tiles.  Uniform forms need no table.
+struct TileTable {
+  int start[kMaxGroups];
+  int count[kMaxGroups];
+  int mt_prefix[kMaxGroups];
+};
+
+// Fills the table (all threads must call) and returns the total number of
+// group m-tiles.  Rows are clamped as documented for device-side values.
+__device__ inline int build_tile_table(const GemmArgs& p, int TM, TileTable& t) {
+  const int G = p.num_groups;
+  if (p.form == kContiguous) {
+    load_clamped_ends(t.mt_prefix, p.group_end, G, p.m_rows);   // reuse as scratch
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+      int e = t.mt_prefix[g];
+      int s = g > 0 ? t.mt_prefix[g - 1] : 0;
+      t.start[g] = s;
+      t.count[g] = e - s;
+    }
+  } else {
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+      int64_t c = p.slot_rows;
+      if (p.form == kMasked) {
+        int64_t v = p.counts[g];
+        c = v < 0 ? 0 : (v > p.slot_rows ? p.slot_rows : v);
+      }
+      t.start[g] = (int)(g * p.slot_rows);
+      t.count[g] = (int)c;
+    }
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) t.mt_prefix[g] = (t.count[g] + TM - 1) / TM;
+  __syncthreads();
+  return block_scan_1024(t.mt_prefix, G, OpAdd(), 0);
+}
+
+// Group owning linear group-m-tile index gm (prefix is inclusive).
+__device__ inline int tile_group(const TileTable& t, int G, int gm) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (t.mt_prefix[mid] > gm) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Four consecutive FP32 results of one output row -> BF16 (nearest even),
+// with the optional bias, written as one 8-byte store.
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v, const uint16_t* bias4) {
+  float f[4] = {v[0], v[1], v[2], v[3]};
+  if (bias4 != nullptr) {
+    uint2 bb = *reinterpret_cast<const uint2*>(bias4);
+    f[0] += bf16_lo(bb.x);
+    f[1] += bf16_hi(bb.x);
+    f[2] += bf16_lo(bb.y);
+    f[3] += bf16_hi(bb.y);
+  }
+  uint2 o;
+  o.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+  o.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = o;
+}
+
+}  // namespace hq

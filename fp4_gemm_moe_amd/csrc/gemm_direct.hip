@@ -1,0 +1,354 @@
+// Direct-load scaled GEMMs: every lane fetches its own MFMA operand slice
+// straight from global memory (no LDS staging), four waves split the K loop
+// and their partial tiles are summed through LDS.
+//
+// This path serves
+//   * skinny M (the decode / small-batch tier of the flashrt/fp4-gemm page's
+//     M-tiered dispatch): the weights stream from HBM once, the tiny A tile is
+//     re-read from cache, and the K split keeps enough waves busy;
+//   * any K with k % 32 == 0 (a lane's K slice is exactly one 32-group, so a
+//     ragged K tail is a per-lane predicate: zero codes, unit scale);
+//   * NVFP4 (UE4M3 scales per 16 cannot be folded into the E8M0-scaled
+//     instruction, so codes are decoded to BF16 -- exactly: an E2M1 value
+//     times a UE4M3 value has at most 6 significant bits -- and multiplied on
+//     the BF16 matrix cores; alpha = g_A * g_B is applied in FP32).
+#include "gemm_common.hpp"
+
+namespace hq {
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves = 4-way K split
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// Resolves linear group-m-tile gm to (group, first row, row end).
+struct TileRows {
+  int g;
+  int64_t row0, row_end;
+};
+
+__device__ __forceinline__ TileRows resolve_tile(const GemmArgs& p, const TileTable& tt, int TM,
+                                                 int mt_per_uniform, int gm) {
+  TileRows t;
+  if (p.form == kUniform) {
+    t.g = gm / mt_per_uniform;
+    int mt = gm - t.g * mt_per_uniform;
+    int64_t gs = (int64_t)t.g * p.slot_rows;
+    t.row0 = gs + (int64_t)mt * TM;
+    int64_t ge = gs + p.slot_rows;
+    t.row_end = t.row0 + TM < ge ? t.row0 + TM : ge;
+  } else {
+    t.g = tile_group(tt, p.num_groups, gm);
+    int mt = gm - (t.g > 0 ? tt.mt_prefix[t.g - 1] : 0);
+    t.row0 = (int64_t)tt.start[t.g] + (int64_t)mt * TM;
+    int64_t ge = (int64_t)tt.start[t.g] + tt.count[t.g];
+    t.row_end = t.row0 + TM < ge ? t.row0 + TM : ge;
+  }
+  return t;
+}
+
+// One lane's operand slice for K step t (128 elements) and its scale byte.
+// FP4: lane group q holds the 32 codes of block 4t + q (16 bytes, dwords
+// 0-3).  FP8: the instruction reads the 32 bytes of lane group q as elements
+// [16q, 16q + 16) (dwords 0-3) and [64 + 16q, 64 + 16q + 16) (dwords 4-7) of
+// the step, while the scale register of lane group q belongs to block
+// [32q, 32q + 32).  Blocks at or past K contribute zero codes (scale 2^0).
+template <int FMT>
+__device__ __forceinline__ void load_slice(const uint8_t* row_codes, const uint8_t* row_sf,
+                                           int t, int q, int kgroups, v8i& frag, int& sc) {
+  const int kg = t * 4 + q;
+  if (FMT == 0) {
+    const uint8_t* base = row_codes + (int64_t)t * 128 + 16 * q;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (t * 4 + (q >> 1) < kgroups) lo = *reinterpret_cast<const uint4*>(base);
+    if (t * 4 + 2 + (q >> 1) < kgroups) hi = *reinterpret_cast<const uint4*>(base + 64);
+    frag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  } else {
+    uint4 lo = make_uint4(0, 0, 0, 0);
+    if (kg < kgroups) lo = *reinterpret_cast<const uint4*>(row_codes + (int64_t)kg * 16);
+    frag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+  }
+  sc = kg < kgroups ? (int)row_sf[kg] : 127;
+}
+
+template <int FMT, int FM, int FN>
+__global__ __launch_bounds__(kThreads) void mx_gemm_direct(GemmArgs p) {
+  constexpr int TM = 16 * FM, TN = 16 * FN;
+  __shared__ TileTable tt;
+  __shared__ v4f red[3][FM * FN][64];
+
+  const int G = p.num_groups;
+  const int NT = (int)((p.n + TN - 1) / TN);
+  const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
+  int total_gm;
+  if (p.form == kUniform) total_gm = G * mt_per;
+  else total_gm = build_tile_table(p, TM, tt);
+  const int total = total_gm * NT;
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kgroups = (int)(p.k / 32);
+  const int ksteps = (kgroups + 3) / 4;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int gm = tile / NT, nt = tile - (tile / NT) * NT;
+    const TileRows tr = resolve_tile(p, tt, TM, mt_per, gm);
+    const int64_t n0 = (int64_t)nt * TN;
+
+    const uint8_t* arow[FM];
+    const uint8_t* asf[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      int64_t r = tr.row0 + fm * 16 + r16;
+      r = r < tr.row_end ? r : tr.row_end - 1;     // rows past the tile end re-read a valid row
+      arow[fm] = p.a + r * p.lda;
+      asf[fm] = p.sfa + r * p.ldsf;
+    }
+    const uint8_t* bg = p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* brow[FN];
+    const uint8_t* bsf[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      int64_t r = n0 + fn * 16 + r16;
+      r = r < p.n ? r : p.n - 1;
+      brow[fn] = bg + r * p.lda;
+      bsf[fn] = bsg + r * p.ldsf;
+    }
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int t = w; t < ksteps; t += 8) {
+      // two K steps per trip (t and t + 4) so twice the loads are in flight
+      v8i af[2][FM], bf[2][FN];
+      int sa[2][FM], sb[2][FN];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) load_slice<FMT>(arow[fm], asf[fm], t + 4 * u, q, kgroups, af[u][fm], sa[u][fm]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) load_slice<FMT>(brow[fn], bsf[fn], t + 4 * u, q, kgroups, bf[u][fn], sb[u][fn]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = mfma_scaled<FMT>(bf[u][fn], af[u][fm], acc[fm][fn], sb[u][fn], sa[u][fm]);
+    }
+
+    if (w > 0) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) red[w - 1][fm * FN + fn][lane] = acc[fm][fn];
+    }
+    __syncthreads();
+    if (w == 0) {
+      const uint16_t* bias = p.bias ? p.bias + (int64_t)tr.g * p.n : nullptr;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int64_t m = tr.row0 + fm * 16 + r16;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          v4f v = acc[fm][fn] + red[0][fm * FN + fn][lane] + red[1][fm * FN + fn][lane] +
+                  red[2][fm * FN + fn][lane];
+          const int64_t n = n0 + fn * 16 + 4 * q;
+          if (m < tr.row_end && n < p.n)
+            store_bf16x4(p.out + m * p.n + n, v, bias ? bias + n : nullptr);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4
+// E2M1 nibble -> FP32 value (exact).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float mag = e == 0 ? (m ? 0.5f : 0.0f) : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return (c & 8u) ? -mag : mag;
+}
+
+// 8 nibbles times one UE4M3 scale -> 8 BF16 (exact: the product has at most
+// 6 significant bits and lies in [2^-10, 2688]).
+__device__ __forceinline__ v8bf decode8(uint32_t w, float sc) {
+  v8s r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (short)(__float_as_uint(e2m1_value((w >> (4 * j)) & 15u) * sc) >> 16);
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// Lane slice for NVFP4: 32 elements [32 kb, 32 kb + 32) of a row (16 bytes)
+// and the two UE4M3 scales of its 16-groups.  The four BF16 MFMAs of one K
+// step consume its elements 8s..8s+7 (s = 0..3); the same K permutation is
+// applied to both operands, so the dot products are unchanged.
+struct NvSlice {
+  uint4 codes;
+  float s0, s1;
+};
+
+__device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8_t* row_sf, int kb,
+                                           bool kin) {
+  NvSlice s;
+  if (kin) {
+    s.codes = *reinterpret_cast<const uint4*>(row_codes + (int64_t)kb * 16);
+    s.s0 = e4m3_value(row_sf[(int64_t)kb * 2] & 0x7Fu);
+    s.s1 = e4m3_value(row_sf[(int64_t)kb * 2 + 1] & 0x7Fu);
+  } else {
+    s.codes = make_uint4(0, 0, 0, 0);
+    s.s0 = s.s1 = 0.0f;
+  }
+  return s;
+}
+
+template <int FM, int FN>
+__global__ __launch_bounds__(kThreads) void nv_gemm_direct(GemmArgs p) {
+  constexpr int TM = 16 * FM, TN = 16 * FN;
+  __shared__ TileTable tt;
+  __shared__ v4f red[3][FM * FN][64];
+
+  const int G = p.num_groups;
+  const int NT = (int)((p.n + TN - 1) / TN);
+  const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
+  int total_gm;
+  if (p.form == kUniform) total_gm = G * mt_per;
+  else total_gm = build_tile_table(p, TM, tt);
+  const int total = total_gm * NT;
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kblocks = (int)(p.k / 32);
+  const int ksteps = (kblocks + 3) / 4;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int gm = tile / NT, nt = tile - (tile / NT) * NT;
+    const TileRows tr = resolve_tile(p, tt, TM, mt_per, gm);
+    const int64_t n0 = (int64_t)nt * TN;
+    const uint8_t* arow[FM];
+    const uint8_t* asf[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      int64_t r = tr.row0 + fm * 16 + r16;
+      r = r < tr.row_end ? r : tr.row_end - 1;
+      arow[fm] = p.a + r * p.lda;
+      asf[fm] = p.sfa + r * p.ldsf;
+    }
+    const uint8_t* bg = p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* brow[FN];
+    const uint8_t* bsf[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      int64_t r = n0 + fn * 16 + r16;
+      r = r < p.n ? r : p.n - 1;
+      brow[fn] = bg + r * p.lda;
+      bsf[fn] = bsg + r * p.ldsf;
+    }
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int t = w; t < ksteps; t += 4) {
+      const int kb = t * 4 + q;
+      const bool kin = kb < kblocks;
+      NvSlice as[FM], bs[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) as[fm] = nv_load(arow[fm], asf[fm], kb, kin);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) bs[fn] = nv_load(brow[fn], bsf[fn], kb, kin);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v8bf ad[FM], bd[FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          uint32_t wd = s == 0 ? as[fm].codes.x : s == 1 ? as[fm].codes.y : s == 2 ? as[fm].codes.z : as[fm].codes.w;
+          ad[fm] = decode8(wd, s < 2 ? as[fm].s0 : as[fm].s1);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          uint32_t wd = s == 0 ? bs[fn].codes.x : s == 1 ? bs[fn].codes.y : s == 2 ? bs[fn].codes.z : bs[fn].codes.w;
+          bd[fn] = decode8(wd, s < 2 ? bs[fn].s0 : bs[fn].s1);
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bd[fn], ad[fm], acc[fm][fn], 0, 0, 0);
+      }
+    }
+
+    if (w > 0) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) red[w - 1][fm * FN + fn][lane] = acc[fm][fn];
+    }
+    __syncthreads();
+    if (w == 0) {
+      const float alpha = p.alpha ? p.alpha[tr.g] : 1.0f;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int64_t m = tr.row0 + fm * 16 + r16;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          v4f v = acc[fm][fn] + red[0][fm * FN + fn][lane] + red[1][fm * FN + fn][lane] +
+                  red[2][fm * FN + fn][lane];
+          v = v * alpha;
+          const int64_t n = n0 + fn * 16 + 4 * q;
+          if (m < tr.row_end && n < p.n) store_bf16x4(p.out + m * p.n + n, v, nullptr);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <class K>
+hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int TN,
+                         const DeviceInfo& dev) {
+  const int64_t NT = (p.n + TN - 1) / TN;
+  int64_t gm_upper;
+  if (p.form == kContiguous) gm_upper = (p.m_rows + TM - 1) / TM + p.num_groups;
+  else gm_upper = (int64_t)p.num_groups * ((p.slot_rows + TM - 1) / TM);
+  int64_t tiles = gm_upper * NT;
+  int cus = dev.num_cus;
+  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+  int64_t grid = (int64_t)cus * 8;
+  if (tiles < grid) grid = tiles;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Direct path entry: picks the tile shape from the rows per group and N.
+hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
+  const int fm = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
+  if (p.mode == kNVFP4) {
+    if (fm == 1) return launch_direct(s, nv_gemm_direct<1, 2>, p, 16, 32, dev);
+    if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2>, p, 32, 32, dev);
+    return launch_direct(s, nv_gemm_direct<4, 2>, p, 64, 32, dev);
+  }
+  if (p.mode == kMXFP8) {
+    if (fm == 1) return launch_direct(s, mx_gemm_direct<0, 1, 1>, p, 16, 16, dev);
+    if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2>, p, 32, 32, dev);
+    return launch_direct(s, mx_gemm_direct<0, 4, 4>, p, 64, 64, dev);
+  }
+  if (fm == 1) return launch_direct(s, mx_gemm_direct<4, 1, 1>, p, 16, 16, dev);
+  if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2>, p, 32, 32, dev);
+  return launch_direct(s, mx_gemm_direct<4, 4, 4>, p, 64, 64, dev);
+}
+
+}  // namespace hq

@@ -1,0 +1,288 @@
+// C-ABI layer: argument validation (host only, before any device work),
+// device checks and dispatch to the kernel launchers.
+//
+// Error convention: flashrt/fp4-gemm page, Notes -- unsupported calls fail
+// before launch and an output is never left silently undefined.  Every check
+// here runs before the first HIP call, so a rejected call touches neither the
+// device nor any output buffer.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "hq.h"
+#include "hq_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hq_status fail(hq_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+hq_status ok() {
+  g_err[0] = '\0';
+  return HQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kI32 = 2147483647LL;
+
+const char* mode_name(int32_t mode) {
+  return mode == HQ_MXFP8 ? "MXFP8" : mode == HQ_MXFP4 ? "MXFP4" : mode == HQ_NVFP4 ? "NVFP4" : "?";
+}
+
+// ---------------------------------------------------------------- device
+struct DevCache {
+  bool probed = false;
+  bool ok = false;
+  hq::DeviceInfo info{};
+};
+std::mutex g_dev_mu;
+DevCache g_dev[64];
+
+hq_status current_device(hq::DeviceInfo* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64)
+    return fail(HQ_ERR_DEVICE, "no usable HIP device (%s)", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevCache& c = g_dev[dev];
+  if (!c.probed) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(HQ_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    c.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    c.info.device = dev;
+    c.info.num_cus = prop.multiProcessorCount;
+    c.info.max_smem = (int)prop.sharedMemPerBlock;
+    c.probed = true;
+    if (!c.ok) {
+      c.probed = true;
+      return fail(HQ_ERR_DEVICE, "device %d is %s; this library is built for gfx950", dev,
+                  prop.gcnArchName);
+    }
+  }
+  if (!c.ok) return fail(HQ_ERR_DEVICE, "device %d is not gfx950", dev);
+  *out = c.info;
+  return HQ_OK;
+}
+
+hq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HQ_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------- GEMM checks
+struct GemmCheck {
+  int32_t mode;
+  const void *a, *sfa, *b, *sfb, *bias, *alpha, *out;
+  int64_t rows, n, k;
+  int64_t groups;
+  const char* what;
+};
+
+// Shape and mode checks common to the GEMM forms.  Returns HQ_OK and sets
+// *noop when there is nothing to compute.
+hq_status check_gemm(const GemmCheck& c, bool* noop) {
+  *noop = false;
+  if (c.mode < HQ_MXFP8 || c.mode > HQ_NVFP4) return fail(HQ_ERR_MODE, "%s: unknown mode %d", c.what, c.mode);
+  if (c.k <= 0 || c.k % 32 != 0) return fail(HQ_ERR_SHAPE, "%s: k=%lld must be a positive multiple of 32", c.what, (long long)c.k);
+  if (c.n < 0 || c.n % 8 != 0) return fail(HQ_ERR_SHAPE, "%s: n=%lld must be a non-negative multiple of 8", c.what, (long long)c.n);
+  if (c.rows < 0) return fail(HQ_ERR_SHAPE, "%s: negative row count", c.what);
+  if (c.rows > kI32 || c.n > kI32 || c.k > kI32)
+    return fail(HQ_ERR_SHAPE, "%s: dimensions must be below 2^31", c.what);
+  // tile ids are 32-bit: (rows/16 + groups) * (n/16) must stay below 2^31
+  if ((c.rows / 16 + c.groups + 1) * (c.n / 16 + 1) > kI32)
+    return fail(HQ_ERR_SHAPE, "%s: problem too large (tile count exceeds 2^31)", c.what);
+  if (c.bias != nullptr && c.mode != HQ_MXFP8)
+    return fail(HQ_ERR_MODE, "%s: bias is only supported in MXFP8 mode (got %s)", c.what, mode_name(c.mode));
+  if (c.mode == HQ_NVFP4 && c.alpha == nullptr && c.rows > 0 && c.n > 0)
+    return fail(HQ_ERR_MODE, "%s: alpha is required in NVFP4 mode", c.what);
+  if (c.mode != HQ_NVFP4 && c.alpha != nullptr)
+    return fail(HQ_ERR_MODE, "%s: alpha is only accepted in NVFP4 mode (got %s)", c.what, mode_name(c.mode));
+  if (c.rows == 0 || c.n == 0) {
+    *noop = true;
+    return HQ_OK;
+  }
+  if (!c.a || !c.sfa || !c.b || !c.sfb || !c.out) return fail(HQ_ERR_NULL, "%s: a, sfa, b, sfb and out are required", c.what);
+  if (!aligned16(c.a) || !aligned16(c.b) || !aligned16(c.out))
+    return fail(HQ_ERR_ALIGN, "%s: a, b and out must be 16-byte aligned", c.what);
+  return HQ_OK;
+}
+
+hq::GemmArgs make_args(int32_t mode, const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                       const uint8_t* sfb, const uint16_t* bias, const float* alpha,
+                       uint16_t* out, int64_t n, int64_t k, int32_t cu_limit) {
+  hq::GemmArgs p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.bias = bias; p.alpha = alpha; p.out = out;
+  p.n = n; p.k = k;
+  p.lda = mode == HQ_MXFP8 ? k : k / 2;
+  p.ldsf = mode == HQ_NVFP4 ? k / 16 : k / 32;
+  p.b_stride = n * p.lda;
+  p.sfb_stride = n * p.ldsf;
+  p.mode = mode;
+  p.cu_limit = cu_limit;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hq_last_error(void) { return g_err; }
+
+hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x, int64_t m, int64_t k,
+                              uint8_t* q, uint8_t* sf, float* global_scale, uint32_t flags) {
+  const char* what = "hq_group_wise_quant";
+  if (mode < HQ_MXFP8 || mode > HQ_NVFP4) return fail(HQ_ERR_MODE, "%s: unknown mode %d", what, mode);
+  if (k <= 0 || k % 32 != 0) return fail(HQ_ERR_SHAPE, "%s: k=%lld must be a positive multiple of 32", what, (long long)k);
+  if (m < 0 || m > kI32 || k > kI32) return fail(HQ_ERR_SHAPE, "%s: m=%lld out of range", what, (long long)m);
+  if (mode != HQ_NVFP4) {
+    if (global_scale != nullptr) return fail(HQ_ERR_MODE, "%s: global_scale is NVFP4 only", what);
+    if (flags != 0) return fail(HQ_ERR_MODE, "%s: flags are NVFP4 only", what);
+  } else {
+    if ((flags & ~HQ_GS_INPUT) != 0) return fail(HQ_ERR_MODE, "%s: unknown flags 0x%x", what, flags);
+    if (global_scale == nullptr) return fail(HQ_ERR_NULL, "%s: NVFP4 needs global_scale", what);
+  }
+  if (m == 0) return ok();
+  if (!x || !q || !sf) return fail(HQ_ERR_NULL, "%s: x, q and sf are required", what);
+  if (!aligned16(x) || !aligned16(q)) return fail(HQ_ERR_ALIGN, "%s: x and q must be 16-byte aligned", what);
+  hq::DeviceInfo dev;
+  hq_status st = current_device(&dev);
+  if (st != HQ_OK) return st;
+  return launched(hq::launch_quant((hipStream_t)stream, mode, x, m, k, q, sf, global_scale,
+                                   (flags & HQ_GS_INPUT) != 0),
+                  what);
+}
+
+hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                        const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                        const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
+                        int32_t cu_limit) {
+  GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, 1, "hq_dense_gemm"};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.form = hq::kUniform;
+  p.num_groups = 1;
+  p.m_rows = m;
+  p.slot_rows = m;
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), c.what);
+}
+
+hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                        const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                        const float* alpha, uint16_t* out, int64_t batch, int64_t m, int64_t n,
+                        int64_t k, int32_t cu_limit) {
+  const char* what = "hq_batch_gemm";
+  if (batch < 0 || batch > kI32) return fail(HQ_ERR_SHAPE, "%s: batch=%lld out of range", what, (long long)batch);
+  if (m < 0 || (batch > 0 && m > kI32 / (batch > 0 ? batch : 1)))
+    return fail(HQ_ERR_SHAPE, "%s: batch * m must be below 2^31", what);
+  GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, batch * m, n, k, batch, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.form = hq::kUniform;
+  p.num_groups = (int32_t)batch;
+  p.m_rows = batch * m;
+  p.slot_rows = m;
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
+}
+
+hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
+                                   const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                   const int32_t* group_end, int32_t num_groups,
+                                   const uint16_t* bias, const float* alpha, uint16_t* out,
+                                   int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
+  const char* what = "hq_group_contiguous_gemm";
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, m_total, n, k, num_groups, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  if (!group_end) return fail(HQ_ERR_NULL, "%s: group_end is required", what);
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.form = hq::kContiguous;
+  p.group_end = group_end;
+  p.num_groups = num_groups;
+  p.m_rows = m_total;
+  p.slot_rows = 0;
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
+}
+
+hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                               const uint8_t* b, const uint8_t* sfb, const int32_t* masked_m,
+                               int32_t num_groups, int64_t max_m_per_group, const uint16_t* bias,
+                               const float* alpha, uint16_t* out, int64_t n, int64_t k,
+                               int32_t cu_limit) {
+  const char* what = "hq_group_masked_gemm";
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  if (max_m_per_group <= 0 || max_m_per_group > kI32 / num_groups)
+    return fail(HQ_ERR_SHAPE, "%s: max_m_per_group=%lld must be > 0 and num_groups * max_m below 2^31",
+                what, (long long)max_m_per_group);
+  GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, num_groups * max_m_per_group, n, k, num_groups, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  if (!masked_m) return fail(HQ_ERR_NULL, "%s: masked_m is required", what);
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.form = hq::kMasked;
+  p.counts = masked_m;
+  p.num_groups = num_groups;
+  p.m_rows = num_groups * max_m_per_group;
+  p.slot_rows = max_m_per_group;
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
+}
+
+hq_status hq_fused_swiglu_quant(void* stream, int32_t mode, const uint16_t* x, int64_t rows,
+                                int64_t h, int32_t num_groups, const int32_t* group_end,
+                                int64_t slot_rows, const int32_t* valid, uint8_t* q, uint8_t* sf,
+                                const float* global_scale, float* y_debug) {
+  const char* what = "hq_fused_swiglu_quant";
+  if (mode < HQ_MXFP8 || mode > HQ_NVFP4) return fail(HQ_ERR_MODE, "%s: unknown mode %d", what, mode);
+  if (h <= 0 || h % 32 != 0 || h > kI32) return fail(HQ_ERR_SHAPE, "%s: h=%lld must be a positive multiple of 32", what, (long long)h);
+  if (rows < 0 || rows > kI32) return fail(HQ_ERR_SHAPE, "%s: rows=%lld out of range", what, (long long)rows);
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  if (group_end == nullptr && slot_rows <= 0)
+    return fail(HQ_ERR_SHAPE, "%s: slot_rows must be > 0 without group_end", what);
+  if (mode == HQ_NVFP4 && global_scale == nullptr) return fail(HQ_ERR_NULL, "%s: NVFP4 needs global_scale", what);
+  if (mode != HQ_NVFP4 && global_scale != nullptr) return fail(HQ_ERR_MODE, "%s: global_scale is NVFP4 only", what);
+  if (rows == 0) return ok();
+  if (!x || !q || !sf) return fail(HQ_ERR_NULL, "%s: x, q and sf are required", what);
+  if (!aligned16(x) || !aligned16(q) || (y_debug && !aligned16(y_debug)))
+    return fail(HQ_ERR_ALIGN, "%s: x, q and y_debug must be 16-byte aligned", what);
+  hq::DeviceInfo dev;
+  hq_status st = current_device(&dev);
+  if (st != HQ_OK) return st;
+  return launched(hq::launch_swiglu_quant((hipStream_t)stream, mode, x, rows, h, num_groups,
+                                          group_end, slot_rows, valid, q, sf, global_scale, y_debug),
+                  what);
+}
+
+}  // extern "C"

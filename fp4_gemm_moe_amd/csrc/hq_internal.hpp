@@ -1,0 +1,60 @@
+// Internal interfaces between the C-ABI layer (hq_api.cpp) and the kernel
+// translation units.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+enum Mode : int32_t { kMXFP8 = 0, kMXFP4 = 1, kNVFP4 = 2 };
+
+// How the rows of a grouped problem are described.
+enum GroupForm : int32_t {
+  kUniform = 0,    // group g owns rows [g*slot_rows, (g+1)*slot_rows)    (dense, batch)
+  kContiguous = 1, // group g owns rows [end[g-1], end[g]), ends clamped  (grouped-contiguous)
+  kMasked = 2,     // group g owns rows g*slot_rows + [0, min(cnt[g], slot_rows))
+};
+
+// One launch of any GEMM form.  Pointers are device pointers; strides are in
+// bytes (codes / scales) or elements (out, bias).
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* sfa;
+  const uint8_t* b;
+  const uint8_t* sfb;
+  const uint16_t* bias;   // [G, n] or nullptr (MXFP8 only)
+  const float* alpha;     // [G] or nullptr (NVFP4 only)
+  uint16_t* out;
+  const int32_t* group_end;  // kContiguous
+  const int32_t* counts;     // kMasked
+  int64_t m_rows;       // rows of a / out (all groups)
+  int64_t slot_rows;    // kUniform / kMasked: rows per group slot
+  int64_t n;
+  int64_t k;            // logical K (elements)
+  int64_t lda;          // bytes per row of a and b (K for FP8, K/2 for FP4)
+  int64_t ldsf;         // scale bytes per row (K/32 or K/16)
+  int64_t b_stride;     // bytes between consecutive groups' weights (n * lda)
+  int64_t sfb_stride;   // n * ldsf
+  int32_t num_groups;
+  int32_t form;
+  int32_t mode;
+  int32_t cu_limit;
+};
+
+struct DeviceInfo {
+  int device;
+  int num_cus;
+  int max_smem;  // bytes of LDS per workgroup
+};
+
+// Returns hipSuccess or the error of the launch.
+hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
+                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input);
+hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64_t rows,
+                               int64_t h, int32_t num_groups, const int32_t* group_end,
+                               int64_t slot_rows, const int32_t* valid, uint8_t* q,
+                               uint8_t* sf, const float* gs, float* y_debug);
+hipError_t launch_gemm(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
+
+}  // namespace hq

@@ -1,0 +1,198 @@
+// Group-wise quantisation of BF16 rows (HALOps "GEMM" page, group_wise_quant
+// section; plain row-major scale layout).
+//
+// Memory-bound: 2 bytes in, 1 (FP8) or 0.5 (FP4) bytes out per element plus
+// one scale byte per group.  Work layout: a flat grid-stride loop over 16-byte
+// chunks of 8 BF16 values.  Because k % 32 == 0, groups never straddle rows,
+// so the [m, k] tensor is processed as one flat array: chunk c covers
+// elements 8c..8c+7, its 32-group is c/4 (MX) or its 16-group is c/2
+// (NVFP4), which is also the flat index of the scale byte.  The lanes of one
+// group are consecutive lanes of a wave, so the group's amax is a DPP
+// reduction over a lane quad (MX) or pair (NVFP4) with no LDS traffic.
+#include "fmt.hpp"
+#include "hq_internal.hpp"
+
+namespace hq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;   // chunks in flight per thread
+
+struct Chunk8 {
+  float f[8];
+};
+
+__device__ __forceinline__ Chunk8 unpack(uint4 v) {
+  Chunk8 c;
+  c.f[0] = bf16_lo(v.x); c.f[1] = bf16_hi(v.x);
+  c.f[2] = bf16_lo(v.y); c.f[3] = bf16_hi(v.y);
+  c.f[4] = bf16_lo(v.z); c.f[5] = bf16_hi(v.z);
+  c.f[6] = bf16_lo(v.w); c.f[7] = bf16_hi(v.w);
+  return c;
+}
+
+__device__ __forceinline__ uint32_t abs_max_bits(const Chunk8& c) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = __float_as_uint(c.f[i]) & 0x7fffffffu;
+    m = a > m ? a : m;
+  }
+  return m;
+}
+
+// MX quantisation of one chunk whose group amax (all 4 lanes) is known.
+// Writes 8 E4M3 bytes or 4 bytes of E2M1 nibbles for chunk index c.
+template <int MODE>
+__device__ __forceinline__ void mx_emit(const Chunk8& c, uint32_t amax, int64_t ci,
+                                        uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  constexpr int EMAX = MODE == kMXFP8 ? 8 : 2;
+  uint32_t sb = mx_scale_byte<EMAX>(amax);
+  float inv = mx_inv_scale(sb);
+  if (MODE == kMXFP8) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w0 |= e4m3_code(c.f[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w1 |= e4m3_code(c.f[4 + i] * inv) << (8 * i);
+    reinterpret_cast<uint2*>(q)[ci] = make_uint2(w0, w1);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(c.f[i] * inv) << (4 * i);
+    reinterpret_cast<uint32_t*>(q)[ci] = w;
+  }
+  if ((ci & 3) == 0) sf[ci >> 2] = (uint8_t)sb;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restrict__ x,
+                                                            int64_t nchunks,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sf) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < nchunks;
+       base += stride * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t ci = base + u * stride;
+      if (ci < nchunks) v[u] = load_nt(&x[ci]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t ci = base + u * stride;
+      // nchunks % 4 == 0 and stride % 4 == 0: a lane quad is all in or all out.
+      if (ci < nchunks) {
+        Chunk8 c = unpack(v[u]);
+        uint32_t amax = quad_max_u32(abs_max_bits(c));
+        mx_emit<MODE>(c, amax, ci, q, sf);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4
+// Global scale g = amax / 2688 (FP32), computed by three tiny launches in
+// stream order: zero the accumulator, reduce |x| into it with atomicMax on the
+// bit pattern (order-preserving for non-negative floats), finalise in place.
+__global__ void nv_amax_zero(uint32_t* acc) { *acc = 0u; }
+
+__global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restrict__ x,
+                                                           int64_t nchunks,
+                                                           uint32_t* __restrict__ acc) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t ci = (int64_t)blockIdx.x * kThreads + threadIdx.x; ci < nchunks; ci += stride) {
+    uint32_t a = abs_max_bits(unpack(load_nt(&x[ci])));
+    m = a > m ? a : m;
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(acc, m);
+}
+
+__global__ void nv_gs_finalize(float* gs) {
+  float a = __uint_as_float(*reinterpret_cast<uint32_t*>(gs));
+  *gs = a == 0.0f ? 1.0f : a / 2688.0f;
+}
+
+// NVFP4: per 16-group (two lanes of 8), sf = UE4M3(amax_b / (6 g)),
+// s_eff = decode(sf) * g, code = E2M1(x / s_eff); IEEE FP32 divisions.
+__device__ __forceinline__ void nv_emit(const Chunk8& c, uint32_t amax_bits, float g, float d,
+                                        int64_t ci, uint8_t* __restrict__ q,
+                                        uint8_t* __restrict__ sf) {
+  float ratio = __uint_as_float(amax_bits) / d;
+  uint32_t sb = e4m3_mag(__float_as_uint(ratio) & 0x7fffffffu);
+  float s_eff = e4m3_value(sb) * g;
+  uint32_t w = 0;
+  if (s_eff != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(c.f[i] / s_eff) << (4 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(c.f[i]) >> 28) & 8u) << (4 * i);
+  }
+  reinterpret_cast<uint32_t*>(q)[ci] = w;
+  if ((ci & 1) == 0) sf[ci >> 1] = (uint8_t)sb;
+}
+
+__global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint4* __restrict__ x,
+                                                            int64_t nchunks,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sf,
+                                                            const float* __restrict__ gs) {
+  const float g = *gs;
+  const float d = 6.0f * g;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < nchunks;
+       base += stride * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t ci = base + u * stride;
+      if (ci < nchunks) v[u] = load_nt(&x[ci]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t ci = base + u * stride;
+      if (ci < nchunks) {
+        Chunk8 c = unpack(v[u]);
+        uint32_t amax = pair_max_u32(abs_max_bits(c));
+        nv_emit(c, amax, g, d, ci, q, sf);
+      }
+    }
+  }
+}
+
+int grid_for(int64_t nchunks, int per_thread) {
+  int64_t blocks = (nchunks + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  if (blocks > 16384) blocks = 16384;
+  return blocks < 1 ? 1 : (int)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
+                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input) {
+  const int64_t nchunks = m * k / 8;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int grid = grid_for(nchunks, kUnroll);
+  if (mode == kMXFP8) {
+    hipLaunchKernelGGL(mx_quant_kernel<kMXFP8>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
+  } else if (mode == kMXFP4) {
+    hipLaunchKernelGGL(mx_quant_kernel<kMXFP4>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
+  } else {
+    if (!gs_input) {
+      uint32_t* acc = reinterpret_cast<uint32_t*>(gs);
+      hipLaunchKernelGGL(nv_amax_zero, dim3(1), dim3(1), 0, s, acc);
+      hipLaunchKernelGGL(nv_amax_kernel, dim3(grid_for(nchunks, 8)), dim3(kThreads), 0, s, xv,
+                         nchunks, acc);
+      hipLaunchKernelGGL(nv_gs_finalize, dim3(1), dim3(1), 0, s, gs);
+    }
+    hipLaunchKernelGGL(nv_quant_kernel, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf,
+                       (const float*)gs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hq

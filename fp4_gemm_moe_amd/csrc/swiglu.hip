@@ -1,0 +1,175 @@
+// Fused SwiGLU + re-quantisation (HALOps "GEMM" page, fused_swiglu_quant
+// section): the row is [gate | up], y = up * silu(gate) = up * gate /
+// (1 + exp(-gate)) in FP32, then y is quantised group-wise exactly as the
+// quantisation kernel does (MXFP8 / MXFP4: UE8M0 per 32; NVFP4: UE4M3 per 16
+// with a supplied global scale).  One pass: BF16 in, codes + scales out.
+//
+// Work layout: each wave owns whole rows (grid-stride over rows), so the
+// row's group membership is decided once per wave; lanes walk the row in
+// 8-element chunks (16-byte loads of gate and of up), and a 32-group is a lane
+// quad (a 16-group a lane pair), reduced with DPP.
+#include "fmt.hpp"
+#include "hq_internal.hpp"
+#include "sched.hpp"
+
+namespace hq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunksPerLane = 3;   // 3 x 64 lanes x 8 = 1536 outputs per pass
+
+struct Y8 {
+  float f[8];
+};
+
+__device__ __forceinline__ float silu_mul(float gate, float up) {
+  // exp(-gate) through the hardware exp2; 1/(1+e) through the hardware
+  // reciprocal.  Large negative gates give e = +Inf and y = 0.
+  float e = __builtin_amdgcn_exp2f(-gate * 1.4426950408889634f);
+  return up * gate * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int MODE>
+__device__ __forceinline__ void emit(const Y8& y, int64_t row, int64_t chunk, int64_t h,
+                                     uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                     float g, float d) {
+  if (MODE == kNVFP4) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a = __float_as_uint(y.f[i]) & 0x7fffffffu;
+      m = a > m ? a : m;
+    }
+    m = pair_max_u32(m);
+    float ratio = __uint_as_float(m) / d;
+    uint32_t sb = e4m3_mag(__float_as_uint(ratio) & 0x7fffffffu);
+    float s_eff = e4m3_value(sb) * g;
+    uint32_t w = 0;
+    if (s_eff != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= e2m1_code(y.f[i] / s_eff) << (4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(y.f[i]) >> 28) & 8u) << (4 * i);
+    }
+    reinterpret_cast<uint32_t*>(q + row * (h / 2))[chunk] = w;
+    if ((chunk & 1) == 0) sf[row * (h / 16) + (chunk >> 1)] = (uint8_t)sb;
+    return;
+  }
+  constexpr int EMAX = MODE == kMXFP8 ? 8 : 2;
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = __float_as_uint(y.f[i]) & 0x7fffffffu;
+    m = a > m ? a : m;
+  }
+  m = quad_max_u32(m);
+  uint32_t sb = mx_scale_byte<EMAX>(m);
+  float inv = mx_inv_scale(sb);
+  if (MODE == kMXFP8) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w0 |= e4m3_code(y.f[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w1 |= e4m3_code(y.f[4 + i] * inv) << (8 * i);
+    reinterpret_cast<uint2*>(q + row * h)[chunk] = make_uint2(w0, w1);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(y.f[i] * inv) << (4 * i);
+    reinterpret_cast<uint32_t*>(q + row * (h / 2))[chunk] = w;
+  }
+  if ((chunk & 3) == 0) sf[row * (h / 32) + (chunk >> 2)] = (uint8_t)sb;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void swiglu_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t h, int32_t G,
+    const int32_t* __restrict__ group_end, int64_t slot_rows, const int32_t* __restrict__ valid,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ sf, const float* __restrict__ gs,
+    float* __restrict__ y_debug) {
+  __shared__ int s_end[kMaxGroups];
+  if (group_end != nullptr) load_clamped_ends(s_end, group_end, G, rows);
+
+  float g = 1.0f, d = 6.0f;
+  if (MODE == kNVFP4) {
+    g = *gs;
+    d = 6.0f * g;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t nchunks = h / 8;   // multiple of 4 because h % 32 == 0
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows;
+       r += waves) {
+    // Is row r processed?  (wave-uniform)
+    int64_t start, grp;
+    if (group_end != nullptr) {
+      grp = find_group(s_end, G, (int)r);
+      if (grp >= G) continue;
+      start = grp > 0 ? s_end[grp - 1] : 0;
+    } else {
+      grp = r / slot_rows;
+      if (grp >= G) continue;
+      start = grp * slot_rows;
+    }
+    if (valid != nullptr) {
+      int64_t c = valid[grp];
+      if (r - start >= c) continue;   // also covers negative counts
+    }
+    const uint4* gate = reinterpret_cast<const uint4*>(x + r * 2 * h);
+    const uint4* up = reinterpret_cast<const uint4*>(x + r * 2 * h + h);
+    for (int64_t base = lane; base < nchunks; base += 64 * kChunksPerLane) {
+      uint4 gv[kChunksPerLane], uv[kChunksPerLane];
+#pragma unroll
+      for (int u = 0; u < kChunksPerLane; ++u) {
+        int64_t c = base + 64 * u;
+        if (c < nchunks) {
+          gv[u] = load_nt(&gate[c]);
+          uv[u] = load_nt(&up[c]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kChunksPerLane; ++u) {
+        int64_t c = base + 64 * u;
+        if (c < nchunks) {
+          Y8 y;
+          const uint32_t gw[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+          const uint32_t uw[4] = {uv[u].x, uv[u].y, uv[u].z, uv[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            y.f[2 * i] = silu_mul(bf16_lo(gw[i]), bf16_lo(uw[i]));
+            y.f[2 * i + 1] = silu_mul(bf16_hi(gw[i]), bf16_hi(uw[i]));
+          }
+          if (y_debug != nullptr) {
+            float4* yd = reinterpret_cast<float4*>(y_debug + r * h + c * 8);
+            yd[0] = make_float4(y.f[0], y.f[1], y.f[2], y.f[3]);
+            yd[1] = make_float4(y.f[4], y.f[5], y.f[6], y.f[7]);
+          }
+          emit<MODE>(y, r, c, h, q, sf, g, d);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64_t rows,
+                               int64_t h, int32_t num_groups, const int32_t* group_end,
+                               int64_t slot_rows, const int32_t* valid, uint8_t* q,
+                               uint8_t* sf, const float* gs, float* y_debug) {
+  int64_t blocks = (rows + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  dim3 grid((unsigned)blocks), block(kThreads);
+#define HQ_SWIGLU(M)                                                                      \
+  hipLaunchKernelGGL(swiglu_quant_kernel<M>, grid, block, 0, s, x, rows, h, num_groups,    \
+                     group_end, slot_rows, valid, q, sf, gs, y_debug)
+  if (mode == kMXFP8) HQ_SWIGLU(kMXFP8);
+  else if (mode == kMXFP4) HQ_SWIGLU(kMXFP4);
+  else HQ_SWIGLU(kNVFP4);
+#undef HQ_SWIGLU
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,190 @@
+/*
+ * hq.h -- C ABI of the MI355X (gfx950) block-scaled low-precision GEMM library.
+ *
+ * The operations follow the HALOps "GEMM" API page (sections group_wise_quant,
+ * dense_gemm, batch_gemm, group_contiguous_gemm, group_masked_gemm,
+ * fused_swiglu_quant), the flashrt/fp4-gemm kernel page (NVFP4 A4W4 GEMM with
+ * BF16 output; unsupported calls fail before launch, output never silently
+ * undefined; calls usable under graph capture) and cuDNN FE "Grouped GEMM +
+ * dGLU (SM100)" (Step 1: the grouped GEMM over cumulative group offsets; the
+ * Data Types table; at most 1024 experts; 16-byte aligned tensors).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *    device).  The caller allocates and owns every buffer; the library never
+ *    allocates, keeps no pointer after a call returns and never synchronises
+ *    the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and is stream-ordered, so a call may be captured into a graph.
+ *  - BF16 values are passed as their uint16_t bit patterns.
+ *  - Quantised operands are K-major and row-major:
+ *        MXFP8: codes uint8 [rows, K]      (E4M3 "fn")
+ *        MXFP4: codes uint8 [rows, K/2]    (E2M1, element 2j in the low nibble
+ *                                           of byte j, element 2j+1 high)
+ *        NVFP4: codes uint8 [rows, K/2]    (E2M1, same packing)
+ *    Scale factors are uint8, plain row-major [rows, K/gs]:
+ *        MXFP8, MXFP4: gs = 32, UE8M0 (byte b means 2^(b-127))
+ *        NVFP4:        gs = 16, UE4M3 (E4M3 bit pattern, sign clear)
+ *    NVFP4 additionally carries one FP32 global scale per tensor; a GEMM takes
+ *    alpha = g_A * g_B.
+ *  - Inputs are const; outputs are written in place and only at valid rows.
+ *  - Every call validates its arguments on the host BEFORE any device work.
+ *    On error nothing is launched and no output byte is written; the status
+ *    is returned and hq_last_error() describes it.
+ *  - Counts and offsets that live in device memory cannot be validated by the
+ *    host.  Kernels clamp them: a masked count to [0, max_m_per_group]; a
+ *    group end to [previous end, m_total].
+ *  - Size limits: k > 0, k % 32 == 0; n % 8 == 0; h % 32 == 0;
+ *    1 <= num_groups <= 1024; row counts < 2^31; m == 0 or n == 0 is a no-op.
+ *    Pointers to x, a, b, q and out must be 16-byte aligned.
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantisation recipe ("w8a8-mxfp8", "w4a4-mxfp4", "w4a4-nvfp4" on the
+ * HALOps page). */
+typedef enum {
+  HQ_MXFP8 = 0,
+  HQ_MXFP4 = 1,
+  HQ_NVFP4 = 2
+} hq_mode;
+
+typedef int32_t hq_status;
+
+#define HQ_OK 0
+#define HQ_ERR_NULL (-1)   /* a required pointer is NULL                    */
+#define HQ_ERR_SHAPE (-2)  /* invalid dimensions                            */
+#define HQ_ERR_ALIGN (-3)  /* a tensor pointer is not 16-byte aligned       */
+#define HQ_ERR_MODE (-4)   /* mode or option combination not allowed        */
+#define HQ_ERR_DEVICE (-5) /* current device is not gfx950 / HIP error      */
+#define HQ_ERR_LAUNCH (-6) /* a kernel launch failed                        */
+
+/* hq_group_wise_quant flags */
+#define HQ_GS_INPUT 1u /* NVFP4: read the global scale from *global_scale   */
+
+/* Thread-local description of the last error of this thread ("" if none). */
+const char* hq_last_error(void);
+
+/*
+ * Group-wise quantisation of BF16 rows (HALOps "GEMM" page, group_wise_quant
+ * section; here always with the plain row-major scale layout).
+ *
+ *   x   [m, k] BF16                         (input)
+ *   q   [m, k] (MXFP8) or [m, k/2] (FP4)    (output codes)
+ *   sf  [m, k/gs]                           (output scales)
+ *
+ * MX modes: per row and 32-group, s = clamp(floor(log2 amax) - emax, -127,
+ * 127) with emax = 8 (E4M3) or 2 (E2M1); sf = s + 127; code = nearest element
+ * of x / 2^s, ties to even, saturating to +-448 / +-6, sign kept (also for
+ * zero).  global_scale must be NULL and flags 0.
+ *
+ * NVFP4: g = amax(x) / 2688 in FP32 (1 if amax == 0), or *global_scale when
+ * flags & HQ_GS_INPUT.  Per 16-group: sf = UE4M3(amax_b / (6 g)), then
+ * code = E2M1(x / (decode(sf) * g)), each division an IEEE FP32 operation
+ * rounded to nearest even (code = +-0 when decode(sf) * g == 0).
+ * global_scale (device float[1]) is required: read when HQ_GS_INPUT is set,
+ * otherwise computed and written (the call then enqueues an amax pass).
+ */
+hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x,
+                              int64_t m, int64_t k, uint8_t* q, uint8_t* sf,
+                              float* global_scale, uint32_t flags);
+
+/*
+ * Dense scaled GEMM (HALOps "GEMM" page, dense_gemm section):
+ *   out[m, n] = bf16( alpha * sum_k deq(a)[m, k] * deq(b)[n, k] + bias[n] )
+ *   a [m, K'] + sfa [m, k/gs];  b [n, K'] + sfb [n, k/gs];  out [m, n] BF16.
+ * bias [n] (BF16) is accepted only in MXFP8 mode (else must be NULL).
+ * alpha (device float[1]) is required in NVFP4 mode and rejected otherwise.
+ * Accumulation is FP32 on the matrix cores; the output is rounded once to
+ * BF16 (nearest even).  cu_limit > 0 caps the compute units used (<= 0: all).
+ */
+hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
+                        const uint8_t* sfa, const uint8_t* b,
+                        const uint8_t* sfb, const uint16_t* bias,
+                        const float* alpha, uint16_t* out, int64_t m,
+                        int64_t n, int64_t k, int32_t cu_limit);
+
+/*
+ * Batch GEMM (HALOps "GEMM" page, batch_gemm section): for every batch item
+ * b, out[b] = a[b] * w[b]^T, with bias[b] / alpha[b].
+ *   a [batch, m, K'], sfa [batch, m, k/gs], b [batch, n, K'],
+ *   sfb [batch, n, k/gs], bias [batch, n], alpha [batch], out [batch, m, n].
+ */
+hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a,
+                        const uint8_t* sfa, const uint8_t* b,
+                        const uint8_t* sfb, const uint16_t* bias,
+                        const float* alpha, uint16_t* out, int64_t batch,
+                        int64_t m, int64_t n, int64_t k, int32_t cu_limit);
+
+/*
+ * Grouped-contiguous GEMM (HALOps "GEMM" page, group_contiguous_gemm section;
+ * cuDNN FE "Grouped GEMM + dGLU (SM100)", Step 1): group g owns rows
+ * [group_end[g-1], group_end[g]) of a (group_end[-1] = 0) and uses
+ * b[g] / sfb[g] / bias[g] / alpha[g].
+ *   a [m_total, K'], sfa [m_total, k/gs], b [num_groups, n, K'],
+ *   sfb [num_groups, n, k/gs], group_end [num_groups] int32 (device,
+ *   cumulative ends, non-decreasing), bias [num_groups, n],
+ *   alpha [num_groups], out [m_total, n].
+ * Any group size (including 0) is allowed.  Rows at or beyond the last end
+ * are not written.  A row map of sorted per-row expert ids converts to
+ * group_end[g] = number of rows with id <= g.
+ */
+hq_status hq_group_contiguous_gemm(void* stream, int32_t mode,
+                                   const uint8_t* a, const uint8_t* sfa,
+                                   const uint8_t* b, const uint8_t* sfb,
+                                   const int32_t* group_end,
+                                   int32_t num_groups, const uint16_t* bias,
+                                   const float* alpha, uint16_t* out,
+                                   int64_t m_total, int64_t n, int64_t k,
+                                   int32_t cu_limit);
+
+/*
+ * Grouped-masked GEMM (HALOps "GEMM" page, group_masked_gemm section): expert
+ * e owns the slot of rows [e * max_m, (e + 1) * max_m); only its first
+ * min(masked_m[e], max_m) rows are computed and written (padded rows are
+ * neither read into a valid output nor written).
+ *   a [num_groups * max_m, K'], sfa [num_groups * max_m, k/gs],
+ *   b [num_groups, n, K'], sfb [num_groups, n, k/gs],
+ *   masked_m [num_groups] int32 (device), bias [num_groups, n],
+ *   alpha [num_groups], out [num_groups * max_m, n].  max_m > 0.
+ */
+hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a,
+                               const uint8_t* sfa, const uint8_t* b,
+                               const uint8_t* sfb, const int32_t* masked_m,
+                               int32_t num_groups, int64_t max_m_per_group,
+                               const uint16_t* bias, const float* alpha,
+                               uint16_t* out, int64_t n, int64_t k,
+                               int32_t cu_limit);
+
+/*
+ * Fused SwiGLU + re-quantisation (HALOps "GEMM" page, fused_swiglu_quant
+ * section): x [rows, 2h] BF16 is [gate | up]; y = up * gate / (1 + exp(-gate))
+ * in FP32 (no intermediate BF16 rounding), then y is quantised group-wise in
+ * `mode` exactly as hq_group_wise_quant does (NVFP4: the global scale is read
+ * from *global_scale, which is then required).
+ *   q [rows, h] (MXFP8) or [rows, h/2]; sf [rows, h/gs].
+ * Row selection: if group_end (device int32 [num_groups]) is given, group g
+ * spans [group_end[g-1], group_end[g]); otherwise group g spans
+ * [g * slot_rows, (g + 1) * slot_rows).  If valid (device int32
+ * [num_groups]) is given only the first min(valid[g], size) rows of each
+ * group are processed, otherwise all of them.  Other rows are not written.
+ * y_debug (optional, device float [rows, h]) receives the FP32 y of the
+ * processed rows: the codes are then exactly the quantisation of y_debug.
+ */
+hq_status hq_fused_swiglu_quant(void* stream, int32_t mode, const uint16_t* x,
+                                int64_t rows, int64_t h, int32_t num_groups,
+                                const int32_t* group_end, int64_t slot_rows,
+                                const int32_t* valid, uint8_t* q, uint8_t* sf,
+                                const float* global_scale, float* y_debug);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H_ */

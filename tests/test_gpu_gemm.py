@@ -1,0 +1,286 @@
+"""GPU parity of the scaled GEMMs (dense, batch, grouped-contiguous,
+grouped-masked) against the oracle.
+
+* Integer-coded inputs (small-integer codes, unit scales) make every product
+  and partial sum exact in FP32, so the result must be bit-exact; this pins
+  the matrix-core lane layout, the scale operand and the output layout.
+* Random inputs: the acceptance bound (2^-7 relative + 1e-3 ||a|| ||b||
+  absolute, relative Frobenius <= 2e-3).
+* Rows a call must not write keep a sentinel; padded rows hold garbage
+  (random codes, 0xFF scales) that must not leak into valid rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_gemm_moe_amd as hq
+import synth
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quant as Q
+from tests import _gpu as U
+from tests.test_oracle_gemm import INT_E2M1, INT_E4M3
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC1   # a BF16 NaN pattern no kernel produces
+
+
+def _int_operand(rng, rows, k, mode, choices):
+    vals = rng.choice(np.array(choices), (rows, k))
+    if mode == "mxfp8":
+        codes = np.vectorize(lambda v: INT_E4M3[abs(v)] | (0x80 if v < 0 else 0))(vals).astype(np.uint8)
+        sf = np.full((rows, k // 32), 127, np.uint8)
+    else:
+        c = np.vectorize(lambda v: INT_E2M1[abs(v)] | (0x8 if v < 0 else 0))(vals).astype(np.uint8)
+        codes = F.pack_nibbles(c)
+        sf = np.full((rows, k // (16 if mode == "nvfp4" else 32)), 0x38 if mode == "nvfp4" else 127, np.uint8)
+    return vals, codes, sf
+
+
+def _quant(bits, mode):
+    if mode == "nvfp4":
+        c, s, g = Q.nvfp4_quant_bf16(bits)
+        return c, s, np.float32(g)
+    c, s = Q.mx_quant_bf16(bits, mode)
+    return c, s, None
+
+
+def _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None):
+    out = torch.full((m, n), 0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_dense_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
+                     out, bias=None if bias is None else U.dev_bf16(bias, dev),
+                     alpha=None if alpha is None else torch.tensor([alpha], dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    return U.host_bits(out)
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("mnk", [(16, 16, 128), (64, 64, 256), (37, 72, 96), (5, 520, 512), (300, 136, 1024)])
+def test_integer_exact_dense(mode, mnk):
+    dev = U.require_gpu()
+    m, n, k = mnk
+    U.banner(f"int-exact dense {mode} m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 1000 + n + k)
+    ch = [-2, -1, 0, 1, 2] if k <= 256 else [-1, 0, 1]
+    av, a, sfa = _int_operand(rng, m, k, mode, ch)
+    bv, b, sfb = _int_operand(rng, n, k, mode, ch)
+    exact = av @ bv.T          # exact in FP32 partial sums; one rounding to BF16 on both sides
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None)
+    want = F.bf16_round(exact.astype(np.float64))
+    assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
+
+
+def test_integer_exact_scales_and_positions():
+    """Distinct power-of-two scales per row and per K-group with one-hot codes:
+    each output picks out exactly one product, exposing any scale/lane mix-up."""
+    dev = U.require_gpu()
+    m, n, k = 32, 32, 256
+    rng = np.random.default_rng(1)
+    a = np.zeros((m, k), np.uint8)
+    b = np.zeros((n, k), np.uint8)
+    hot_a = rng.integers(0, k, m)
+    hot_b = hot_a[rng.integers(0, m, n)]
+    a[np.arange(m), hot_a] = 0x38           # 1.0 in E4M3
+    b[np.arange(n), hot_b] = 0x40           # 2.0
+    sfa = rng.integers(120, 134, (m, k // 32)).astype(np.uint8)
+    sfb = rng.integers(120, 134, (n, k // 32)).astype(np.uint8)
+    got = _dense_gpu("mxfp8", a, sfa, b, sfb, m, n, k, dev)
+    want = G.dense_gemm("mxfp8", a, sfa, b, sfb)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+def test_dense_random_small(mode):
+    dev = U.require_gpu()
+    d = synth.dense_mxfp8_256()
+    for (m, n, k) in [(256, 256, 256), (33, 40, 160), (1, 64, 512), (16, 136, 4096)]:
+        U.banner(f"dense {mode} m={m} n={n} k={k}")
+        rng = np.random.default_rng(m + n + k)
+        xa = d["a"][:m, :k] if (m, k) == (256, 256) else synth.normal_bf16(rng, (m, k))
+        xb = d["b"][:n, :k] if (n, k) == (256, 256) else synth.normal_bf16(rng, (n, k), 0.5)
+        a, sfa, ga = _quant(xa, mode)
+        b, sfb, gb = _quant(xb, mode)
+        alpha = None if ga is None else np.float32(ga * gb)
+        got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=alpha)
+        want = G.dense_gemm(mode, a, sfa, b, sfb, alpha=alpha)
+        U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"{mode} {m}x{n}x{k}")
+
+
+def test_config0_dense_mxfp8_256_with_gpu_quant():
+    """256^3 MXFP8, seed 0: quantised on the GPU (bit-exact to the oracle),
+    then the GEMM within tolerance."""
+    dev = U.require_gpu()
+    d = synth.dense_mxfp8_256()
+    qa, sa, _ = hq.quantize(U.dev_bf16(d["a"], dev), "mxfp8")
+    qb, sb, _ = hq.quantize(U.dev_bf16(d["b"], dev), "mxfp8")
+    out = torch.empty(256, 256, dtype=torch.bfloat16, device=dev)
+    hq.hq_dense_gemm("mxfp8", qa, sa, qb, sb, out)
+    torch.cuda.synchronize()
+    a, sfa = Q.mx_quant_bf16(d["a"], "mxfp8")
+    b, sfb = Q.mx_quant_bf16(d["b"], "mxfp8")
+    assert np.array_equal(U.host_u8(qa), a) and np.array_equal(U.host_u8(sb), sfb)
+    want = G.dense_gemm("mxfp8", a, sfa, b, sfb)
+    U.assert_gemm_close(U.host_bits(out), want, U.deq("mxfp8", a, sfa), U.deq("mxfp8", b, sfb))
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_config1_batch_mxfp8(with_bias):
+    dev = U.require_gpu()
+    d = synth.batch_mxfp8()
+    Bn, m, k = d["a"].shape
+    n = d["b"].shape[1]
+    a, sfa = Q.mx_quant_bf16(d["a"].reshape(Bn * m, k), "mxfp8")
+    b, sfb = Q.mx_quant_bf16(d["b"].reshape(Bn * n, k), "mxfp8")
+    bias = d["bias"] if with_bias else None
+    out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
+    U.banner(f"batch mxfp8 bias={with_bias}")
+    hq.hq_batch_gemm("mxfp8", U.dev_u8(a, dev).view(Bn, m, k), U.dev_u8(sfa, dev).view(Bn, m, -1),
+                     U.dev_u8(b, dev).view(Bn, n, k), U.dev_u8(sfb, dev).view(Bn, n, -1), out,
+                     bias=None if bias is None else U.dev_bf16(bias, dev))
+    torch.cuda.synchronize()
+    want = G.batch_gemm("mxfp8", a.reshape(Bn, m, k), sfa.reshape(Bn, m, -1), b.reshape(Bn, n, k),
+                        sfb.reshape(Bn, n, -1), bias=bias)
+    got = U.host_bits(out)
+    for i in range(Bn):
+        U.assert_gemm_close(got[i], want[i], U.deq("mxfp8", a[i * m:(i + 1) * m], sfa[i * m:(i + 1) * m]),
+                            U.deq("mxfp8", b[i * n:(i + 1) * n], sfb[i * n:(i + 1) * n]), what=f"batch {i}")
+
+
+def test_config1_dense_mxfp4_32x512x256():
+    dev = U.require_gpu()
+    d = synth.dense_mxfp4_small()
+    a, sfa = Q.mx_quant_bf16(d["a"], "mxfp4")
+    b, sfb = Q.mx_quant_bf16(d["b"], "mxfp4")
+    got = _dense_gpu("mxfp4", a, sfa, b, sfb, 32, 512, 256, dev)
+    want = G.dense_gemm("mxfp4", a, sfa, b, sfb)
+    U.assert_gemm_close(got, want, U.deq("mxfp4", a, sfa), U.deq("mxfp4", b, sfb))
+
+
+def _grouped_inputs(mode, counts, K, N, seed, trailing=0):
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    ends = np.cumsum(counts).astype(np.int32)
+    R = int(ends[-1]) + trailing
+    xa = synth.normal_bf16(rng, (R, K))
+    xb = synth.normal_bf16(rng, (E * N, K), 0.05)
+    a, sfa, ga = _quant(xa, mode)
+    bq, bs, gb = _quant(xb, mode)
+    b = bq.reshape(E, N, -1)
+    sfb = bs.reshape(E, N, -1)
+    return ends, a, sfa, b, sfb, ga, gb
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("case", ["ragged", "aligned"])
+def test_group_contiguous(mode, case):
+    dev = U.require_gpu()
+    if case == "ragged":
+        counts, K, N, trailing = [7, 0, 33, 1, 160, 0, 17], 96, 40, 9
+    else:
+        counts, K, N, trailing = [128, 256, 0, 384], 512, 256, 0
+    U.banner(f"contiguous {mode} {case}")
+    ends, a, sfa, b, sfb, ga, gb = _grouped_inputs(mode, counts, K, N, 42, trailing)
+    E = len(counts)
+    R = a.shape[0]
+    alpha = None if ga is None else np.full(E, np.float32(ga * gb), np.float32)
+    bias = synth.normal_bf16(np.random.default_rng(3), (E, N), 0.1) if mode == "mxfp8" else None
+    out = torch.full((R, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_group_contiguous_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev),
+                                U.dev_u8(sfb, dev), U.dev_i32(ends, dev), out,
+                                bias=None if bias is None else U.dev_bf16(bias, dev),
+                                alpha=None if alpha is None else torch.from_numpy(alpha).to(dev))
+    torch.cuda.synchronize()
+    got = U.host_bits(out)
+    want, written = G.group_contiguous_gemm(mode, a, sfa, b, sfb, ends, bias=bias, alpha=alpha,
+                                            out=np.full((R, N), SENTINEL, np.uint16))
+    assert np.all(got[~written] == SENTINEL), "rows outside every group were written"
+    starts = np.concatenate([[0], ends[:-1]])
+    for g in range(E):
+        lo, hi = int(starts[g]), int(ends[g])
+        if hi > lo:
+            U.assert_gemm_close(got[lo:hi], want[lo:hi], U.deq(mode, a[lo:hi], sfa[lo:hi]),
+                                U.deq(mode, b[g], sfb[g]), None if alpha is None else alpha[g], f"group {g}")
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+def test_group_masked_matches_contiguous_with_garbage_padding(mode):
+    dev = U.require_gpu()
+    E, Mmax, K, N = 6, 48, 256, 64
+    counts = np.array([48, 0, 13, 1, 30, 47], np.int32)
+    rng = np.random.default_rng(9)
+    U.banner(f"masked {mode}")
+    xa = synth.normal_bf16(rng, (int(counts.sum()), K))
+    a_c, sfa_c, ga = _quant(xa, mode)
+    xb = synth.normal_bf16(rng, (E * N, K), 0.05)
+    bq, bs, gb = _quant(xb, mode)
+    b, sfb = bq.reshape(E, N, -1), bs.reshape(E, N, -1)
+    # padded layout: garbage codes and 0xFF (NaN) scales in every padded row
+    a_m = synth.garbage_bytes(1, (E * Mmax, a_c.shape[1]))
+    sfa_m = np.full((E * Mmax, sfa_c.shape[1]), 0xFF, np.uint8)
+    ends = np.cumsum(counts)
+    starts = ends - counts
+    for e in range(E):
+        a_m[e * Mmax:e * Mmax + counts[e]] = a_c[starts[e]:ends[e]]
+        sfa_m[e * Mmax:e * Mmax + counts[e]] = sfa_c[starts[e]:ends[e]]
+    alpha = None if ga is None else torch.full((E,), float(np.float32(ga * gb)), dtype=torch.float32, device=dev)
+    out_m = torch.full((E * Mmax, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_group_masked_gemm(mode, U.dev_u8(a_m, dev), U.dev_u8(sfa_m, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
+                            U.dev_i32(counts, dev), out_m, Mmax, alpha=alpha)
+    out_c = torch.full((len(xa), N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_group_contiguous_gemm(mode, U.dev_u8(a_c, dev), U.dev_u8(sfa_c, dev), U.dev_u8(b, dev),
+                                U.dev_u8(sfb, dev), U.dev_i32(ends, dev), out_c, alpha=alpha)
+    torch.cuda.synchronize()
+    gm, gc = U.host_bits(out_m), U.host_bits(out_c)
+    al = None if alpha is None else np.full(E, np.float32(ga * gb), np.float32)
+    for e in range(E):
+        blk = gm[e * Mmax:(e + 1) * Mmax]
+        assert np.all(blk[counts[e]:] == SENTINEL), f"expert {e}: padded rows written"
+        assert np.array_equal(blk[:counts[e]], gc[starts[e]:ends[e]]), f"expert {e}: masked != contiguous"
+        if counts[e]:
+            want = G.dense_gemm(mode, a_c[starts[e]:ends[e]], sfa_c[starts[e]:ends[e]], b[e], sfb[e],
+                                alpha=None if al is None else al[e])
+            U.assert_gemm_close(blk[:counts[e]], want, U.deq(mode, a_c[starts[e]:ends[e]], sfa_c[starts[e]:ends[e]]),
+                                U.deq(mode, b[e], sfb[e]), None if al is None else al[e], f"expert {e}")
+
+
+def test_device_counts_are_clamped():
+    """Out-of-range device values: a masked count above max_m covers the slot
+    exactly; a negative count covers nothing; decreasing ends give empty
+    groups; ends beyond m_total stop at m_total."""
+    dev = U.require_gpu()
+    K, N, Mmax = 128, 32, 16
+    rng = np.random.default_rng(2)
+    xa = synth.normal_bf16(rng, (3 * Mmax, K))
+    a, sfa = Q.mx_quant_bf16(xa, "mxfp8")
+    xb = synth.normal_bf16(rng, (3 * N, K), 0.1)
+    bq, bs = Q.mx_quant_bf16(xb, "mxfp8")
+    b, sfb = bq.reshape(3, N, K), bs.reshape(3, N, -1)
+    counts = np.array([1000, -5, 3], np.int32)
+    out = torch.full((3 * Mmax, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    U.banner("clamp masked")
+    hq.hq_group_masked_gemm("mxfp8", U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
+                            U.dev_i32(counts, dev), out, Mmax)
+    torch.cuda.synchronize()
+    want, written = G.group_masked_gemm("mxfp8", a, sfa, b, sfb, counts, Mmax,
+                                        out=np.full((3 * Mmax, N), SENTINEL, np.uint16))
+    got = U.host_bits(out)
+    assert np.all(got[~written] == SENTINEL)
+    for e, c in [(0, Mmax), (2, 3)]:
+        lo, hi = e * Mmax, e * Mmax + c
+        assert written[lo:hi].all()
+        U.assert_gemm_close(got[lo:hi], want[lo:hi], U.deq("mxfp8", a[lo:hi], sfa[lo:hi]),
+                            U.deq("mxfp8", b[e], sfb[e]), what=f"clamped expert {e}")
+    ends = np.array([20, 10, 999], np.int32)
+    out2 = torch.full((3 * Mmax, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    U.banner("clamp contiguous")
+    hq.hq_group_contiguous_gemm("mxfp8", U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev),
+                                U.dev_u8(sfb, dev), U.dev_i32(ends, dev), out2)
+    torch.cuda.synchronize()
+    want2, written2 = G.group_contiguous_gemm("mxfp8", a, sfa, b, sfb, ends,
+                                              out=np.full((3 * Mmax, N), SENTINEL, np.uint16))
+    got2 = U.host_bits(out2)
+    assert written2.all()
+    for lo, hi, g in [(0, 20, 0), (20, 48, 2)]:
+        U.assert_gemm_close(got2[lo:hi], want2[lo:hi], U.deq("mxfp8", a[lo:hi], sfa[lo:hi]),
+                            U.deq("mxfp8", b[g], sfb[g]), what=f"clamped group {g}")

@@ -1,0 +1,111 @@
+"""GPU parity of hq_group_wise_quant against the oracle: codes, scale bytes
+and the NVFP4 global scale must be bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_gemm_moe_amd as hq
+import synth
+from oracle import quant as Q
+from tests import _gpu as U
+from tests.test_oracle_quant import _random_bf16_blocks
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["mxfp8", "mxfp4", "nvfp4"]
+
+
+def _run(mode, bits, dev, g=None):
+    x = U.dev_bf16(bits, dev)
+    gs = None
+    if mode == "nvfp4" and g is not None:
+        gs = torch.tensor([g], dtype=torch.float32, device=dev)
+    q, sf, gout = hq.quantize(x, mode, gs)
+    torch.cuda.synchronize()
+    return U.host_u8(q), U.host_u8(sf), (None if gout is None else float(gout.cpu()[0]))
+
+
+def _oracle(mode, bits, g=None):
+    if mode == "nvfp4":
+        c, s, gg = Q.nvfp4_quant_bf16(bits, None if g is None else np.float32(g))
+        return c, s, float(gg)
+    c, s = Q.mx_quant_bf16(bits, mode)
+    return c, s, None
+
+
+def _check(mode, bits, dev, g=None, what=""):
+    U.banner(f"quant {mode} {bits.shape} {what}")
+    qc, qs, qg = _run(mode, bits, dev, g)
+    oc, os_, og = _oracle(mode, bits, g)
+    assert np.array_equal(qs, os_), f"{mode} {what}: {np.sum(qs != os_)} scale bytes differ"
+    assert np.array_equal(qc, oc), f"{mode} {what}: {np.sum(qc != oc)} code bytes differ"
+    if mode == "nvfp4":
+        assert np.float32(qg) == np.float32(og), (qg, og)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quant_dense_256(mode):
+    dev = U.require_gpu()
+    d = synth.dense_mxfp8_256()
+    _check(mode, d["a"], dev, what="256x256 N(0,1)")
+    _check(mode, d["b"], dev, what="256x256 N(0,1) B")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(1, 32), (37, 96), (129, 544), (1024, 256)])
+def test_quant_ragged_shapes(mode, shape):
+    dev = U.require_gpu()
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    bits = synth.normal_bf16(rng, shape, 3.0)
+    _check(mode, bits, dev, what="ragged")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_quant_adversarial_blocks(mode):
+    """Zeros, negative zeros, BF16 subnormals, exact grid midpoints, outliers,
+    values at the top of a binade."""
+    dev = U.require_gpu()
+    rng = np.random.default_rng(77)
+    bits = _random_bf16_blocks(rng, 64, 512)
+    if mode == "nvfp4":
+        bits[(bits & 0x7F80) == 0] = 0   # NVFP4 recipe is defined on normal BF16 inputs
+    _check(mode, bits, dev, what="adversarial")
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4"])
+def test_quant_every_bf16_value(mode):
+    """Every finite BF16 pattern, shuffled into 32-groups, so every element
+    value meets many different group scales."""
+    dev = U.require_gpu()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = (bits & 0x7F80) != 0x7F80
+    vals = bits[fin]
+    rng = np.random.default_rng(5)
+    out = np.concatenate([rng.permutation(vals) for _ in range(3)])
+    out = out[: (len(out) // 32) * 32].reshape(-1, 32 * 8)[: 4096]
+    _check(mode, np.ascontiguousarray(out), dev, what="all finite BF16")
+
+
+def test_quant_nvfp4_supplied_global_scale():
+    dev = U.require_gpu()
+    rng = np.random.default_rng(3)
+    bits = synth.normal_bf16(rng, (64, 256), 1.0)
+    _check("nvfp4", bits, dev, g=0.0012345, what="supplied g")
+    zeros = np.zeros((4, 64), np.uint16)
+    _check("nvfp4", zeros, dev, what="all zero -> g = 1")
+
+
+def test_quant_large_activation_sample():
+    """MoE activation quantisation at full size [65536, 4096] (MXFP8): every
+    scale byte and a sample of code rows against the oracle."""
+    dev = U.require_gpu()
+    rng = np.random.default_rng(31)
+    m, k = 65536, 4096
+    U.banner("quant mxfp8 65536x4096 (sampled rows)")
+    x = torch.randn(m, k, generator=torch.Generator(device=dev).manual_seed(31), device=dev).to(torch.bfloat16)
+    q, sf, _ = hq.quantize(x, "mxfp8")
+    rows = np.sort(rng.choice(m, 512, replace=False))
+    xb = U.host_bits(x[torch.from_numpy(rows).to(dev)])
+    oc, os_ = Q.mx_quant_bf16(xb, "mxfp8")
+    assert np.array_equal(U.host_u8(sf[torch.from_numpy(rows).to(dev)]), os_)
+    assert np.array_equal(U.host_u8(q[torch.from_numpy(rows).to(dev)]), oc)
