@@ -1,11 +1,20 @@
-// GEMM dispatch by mode, form and shape.
+// GEMM dispatch by mode, form and shape (the M-tiered dispatch of the
+// flashrt/fp4-gemm page, re-chosen for gfx950):
+//   * MX modes with K a multiple of the 128-byte K step and more than 16 rows
+//     per group: the LDS-tiled persistent kernel;
+//   * skinny M (<= 16 rows per group), any other K, and NVFP4: the direct
+//     kernel.
 #include "gemm_common.hpp"
 
 namespace hq {
 
 hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev);
+hipError_t launch_gemm_tiled(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev);
+bool tiled_supported(const GemmArgs& p);
 
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
+  if (rows_hint > 16 && tiled_supported(p)) return launch_gemm_tiled(s, p, dev);
   return launch_gemm_direct(s, p, dev);
 }
 
