@@ -150,36 +150,42 @@ def run_moe(args, torch, hq, synth):
 
 
 def cpu_baseline_moe(ctx, budget_s=12.0):
-    """The oracle on a bounded sample of the same step: the first S routed rows
-    of expert 0 (quantise, GEMM against expert 0's weights, SwiGLU +
-    re-quantise).  Expert 0's weights are quantised by the oracle before the
-    clock starts, like the device path's static weights."""
+    """The oracle on a bounded sample of the same step: the routed rows of
+    experts 0, 1, 2, ... (quantise, GEMM against the expert's weights, SwiGLU +
+    re-quantise) until about budget_s seconds of CPU work.  Each expert's
+    weights are quantised by the oracle before its clock starts, like the
+    device path's static weights."""
     from oracle import gemm as G
     from oracle import quant as Q
     from oracle import swiglu as S
     K, N, H = ctx["K"], ctx["N"], ctx["H"]
-    w, wsf = Q.mx_quant_bf16(ctx["b"][0], "mxfp8")
-    rows = 8
-    spent = 0.0
-    while True:
-        xa = ctx["a"][:rows]
+    counts, ends = ctx["counts"], ctx["ends"]
+    starts = np.concatenate([[0], ends[:-1]]).astype(np.int64)
+    spent, rows_done, experts = 0.0, 0, 0
+    for g in range(len(counts)):
+        c = int(counts[g])
+        if c == 0:
+            continue
+        w, wsf = Q.mx_quant_bf16(ctx["b"][g], "mxfp8")
+        xa = ctx["a"][starts[g]:starts[g] + c]
         t0 = time.perf_counter()
         a, sfa = Q.mx_quant_bf16(xa, "mxfp8")
         out = G.dense_gemm("mxfp8", a, sfa, w, wsf)
         S.swiglu_quant(out, H, "mxfp8")
-        spent = time.perf_counter() - t0
-        if spent > budget_s / 4 or rows >= int(ctx["counts"][0]):
+        spent += time.perf_counter() - t0
+        rows_done += c
+        experts += 1
+        if spent >= budget_s:
             break
-        rows = min(rows * 4, int(ctx["counts"][0]))
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    tflops = 2.0 * rows * N * K / spent / 1e12
+    tflops = 2.0 * rows_done * N * K / spent / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} routed rows of expert 0 (quant + GEMM vs expert 0 + SwiGLU/quant), "
-                      f"{spent:.2f} s"}
+            "sample": f"routed rows of the first {experts} non-empty experts ({rows_done} of "
+                      f"{int(counts.sum())} rows): MXFP8 quant + GEMM + SwiGLU/quant, {spent:.1f} s"}
 
 
 # ---------------------------------------------------------------- other workloads
@@ -261,6 +267,9 @@ def main():
     ap.add_argument("--n", type=int, default=17408)
     ap.add_argument("--k", type=int, default=5120)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -277,6 +286,15 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
+    if args.copy_probe_mb > 0:
+        nbytes = args.copy_probe_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nbytes} bytes read and written once")
+        del src, dst
     runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4}[args.workload]
     value, ms_step, cfg, roof, kernels, ctx = runner(args, torch, hq, synth)
     cpu = None
