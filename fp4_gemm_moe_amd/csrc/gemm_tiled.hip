@@ -4,49 +4,49 @@
 // group_masked_gemm, batch_gemm sections).
 //
 // Structure (gfx950):
-//   * 256 threads = 4 waves in a 2 x 2 grid; a block tile is BM x BN output
-//     elements, a wave tile (BM/2) x (BN/2) built from 16 x 16 fragments of
-//     V_MFMA_SCALE_F32_16X16X128_F8F6F4 (weights as src0, activations as
-//     src1, FP32 accumulation, E8M0 scales per 32-element block).
-//   * One K step moves 128 bytes of every row: 128 FP8 elements (one MFMA
-//     step) or 256 FP4 elements (two MFMA steps).  A lane reads 16-byte
-//     chunks q and q + 4 of its fragment row in both cases, so the LDS read
-//     pattern is format independent.
-//   * Global -> LDS with 16-byte direct-to-LDS loads (no register staging).
-//     A wave's load writes 1 KB of LDS = 8 rows; lane j fetches the chunk that
-//     belongs at LDS slot j, so the XOR swizzle (chunk ^ ((row ^ row>>3) & 7))
-//     costs nothing and fragment reads are bank-conflict free.
-//   * Two LDS stages: the loads of step k+1 are in flight while step k is
-//     multiplied.
-//   * Persistent grid (one workgroup per compute unit).  Tiles are ordered so
-//     that the 32 consecutive tiles that one XCD (one L2) runs side by side
-//     cover 4 row tiles x 8 column tiles: A and B tiles are shared through
-//     the L2 instead of being fetched 32 times.
+//   * 256 threads = 4 waves (one per SIMD) in a 2 x 2 grid; a block tile is
+//     256 x 256 outputs, a wave tile 128 x 128 built from 4 x 4 fragments of
+//     V_MFMA_SCALE_F32_32X32X64_F8F6F4 (weights as src0, activations as src1,
+//     FP32 accumulation in 256 accumulation registers, E8M0 scales per 32
+//     elements).  A 128 x 128 wave tile keeps the LDS fragment traffic at
+//     1/128 byte per FLOP, which the LDS can serve at the matrix-core rate.
+//   * A stage holds 128 bytes of every row of the A and B tiles: 128 FP8
+//     elements (two MFMA steps of 64) or 256 FP4 elements (four steps).  In
+//     both formats a lane reads 16-byte chunks h, 2+h, 4+h, 6+h of its
+//     fragment row (h = lane / 32): FP8 pairs them as (h, 2+h), (4+h, 6+h);
+//     FP4 uses each chunk as one step.
+//   * Global -> LDS with 16-byte direct-to-LDS loads into an XOR-swizzled
+//     layout; a wave's load fills 1 KB = 8 rows, lane j fetching the chunk
+//     that belongs at slot j.
+//   * Two LDS stages: the loads of step k+1 fly during step k, and the loads
+//     of the first step of the workgroup's next tile fly during the last step
+//     of the current tile, ahead of its epilogue stores.  Vector-memory
+//     operations retire in issue order, so every wait names how many later
+//     operations may stay in flight and the stores drain under the next
+//     tile's first step.
+//   * Persistent grid, one workgroup per compute unit.  Tiles are ordered so
+//     that the 32 consecutive tiles one XCD (one L2) runs side by side cover
+//     4 row tiles x 8 column tiles.
 // Requirements (checked by the dispatcher): K % 128 == 0 (FP8) or
-// K % 256 == 0 (FP4), scale rows 4-byte aligned.
+// K % 256 == 0 (FP4); scale pointers 4-byte aligned; lda * 256 < 2^31;
+// n * 512 < 2^31.
 #include "gemm_common.hpp"
 
 namespace hq {
 namespace {
 
-constexpr int kThreads = 256;
-
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) const void* lds_cptr_t;
 
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row; conflict
+// free for the fragment reads below (32 rows x one chunk per half wave),
+// measured with the LDS bank-conflict counter.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// 32-bit LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_cptr_t)p;
 }
 
-// Direct-to-LDS loads: every lane fetches `size` bytes from sbase + voff and
-// the wave's 64 results land contiguously at LDS address m0 (lane j at
-// m0 + j * size).  Issued as inline assembly so that the compiler inserts no
-// alias waits of its own: the kernel orders these writes explicitly (wait for
-// the vector-memory counter, then a workgroup barrier, before a stage is read;
-// a barrier after the last read of a stage before it is refilled).  m0 is set
-// inside each statement; nothing else in the kernel uses it.
 // A pointer the compiler cannot prove uniform (it came through LDS), made
 // uniform explicitly; the value is the same in every lane.
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
@@ -56,6 +56,13 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Direct-to-LDS loads: every lane fetches `size` bytes from sbase + voff and
+// the wave's 64 results land contiguously at LDS address m0 (lane j at
+// m0 + j * size).  Issued as inline assembly so that the compiler inserts no
+// alias waits of its own: the kernel orders these writes explicitly (a wait
+// on the vector-memory counter, then a workgroup barrier, before a stage is
+// read; a barrier after the last read of a stage before it is refilled).  m0
+// is set inside each statement; nothing else in the kernel uses it.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "s"(lds) : "memory");
@@ -68,232 +75,349 @@ __device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+__device__ __forceinline__ uint32_t lds_read4(const uint8_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
 
-template <int FMT, int BM, int BN>
-struct TiledCfg {
-  static constexpr int SB = FMT == 0 ? 4 : 8;          // scale bytes per row per K step
-  static constexpr int PLANES = SB / 4;                  // dword planes of scales
-  static constexpr int A_BYTES = BM * 128;
-  static constexpr int B_BYTES = BN * 128;
-  static constexpr int SA_BYTES = BM * SB;
-  static constexpr int SBB_BYTES = BN * SB;
-  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SBB_BYTES;
-  static constexpr int FM = BM / 32;                     // fragments per wave (rows)
-  static constexpr int FN = BN / 32;                     // fragments per wave (cols)
-  static constexpr int A_LOADS = BM / 32;                // 16-byte loads per thread per K step
-  static constexpr int B_LOADS = BN / 32;
+template <int FMT>
+__device__ __forceinline__ v16f mfma32(v8i w, v8i x, v16f acc, int sw, int sx) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, acc, FMT, FMT, 0, sw, 0, sx);
+}
+
+constexpr int BM = 256, BN = 256;
+constexpr int WAVES = 4;
+constexpr int THREADS = WAVES * 64;
+constexpr int WT = 128;                     // wave tile (square)
+constexpr int SROW = 128;                   // bytes of a row per stage
+constexpr int LOADS = BM * (SROW / 16) / THREADS;   // 16-byte loads per operand per thread (8)
+constexpr int kStores = 32;                 // output stores per thread per tile
+
+template <int FMT>
+struct Cfg {
+  static constexpr int SB = FMT == 0 ? 4 : 8;       // scale bytes per row per stage
+  static constexpr int PLANES = SB / 4;
+  static constexpr int A_BYTES = BM * SROW;
+  static constexpr int B_BYTES = BN * SROW;
+  static constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * SB;
+  static constexpr int OPS = 2 * LOADS + 2 * PLANES;  // vector-memory ops per stage per thread
 };
 
-template <int FMT, int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void mx_gemm_tiled(GemmArgs p) {
-  using C = TiledCfg<FMT, BM, BN>;
+// Where a tile sits: group, first row, row end and first column.
+struct TileGeom {
+  int g;
+  int64_t row0, row_end, n0;
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const GemmArgs& p, const TileTable& tt, int total_gm,
+                                              int NT, int mt_per, int t) {
+  // blocks of 4 m-tiles x all n-tiles, walked n-major inside the block so 32
+  // consecutive tiles = 4 m x 8 n
+  const int blk = t / (4 * NT);
+  const int rem = t - blk * 4 * NT;
+  const int mrem = total_gm - blk * 4;
+  const int mb = mrem < 4 ? mrem : 4;
+  const int nt = rem / mb;
+  const int gm = blk * 4 + (rem - nt * mb);
+  TileGeom tg;
+  if (p.form == kUniform) {
+    tg.g = gm / mt_per;
+    int mt = gm - tg.g * mt_per;
+    int64_t gs = (int64_t)tg.g * p.slot_rows;
+    tg.row0 = gs + (int64_t)mt * BM;
+    tg.row_end = tg.row0 + BM < gs + p.slot_rows ? tg.row0 + BM : gs + p.slot_rows;
+  } else {
+    tg.g = tile_group(tt, p.num_groups, gm);
+    int mt = gm - (tg.g > 0 ? tt.mt_prefix[tg.g - 1] : 0);
+    tg.row0 = (int64_t)tt.start[tg.g] + (int64_t)mt * BM;
+    int64_t ge = (int64_t)tt.start[tg.g] + tt.count[tg.g];
+    tg.row_end = tg.row0 + BM < ge ? tg.row0 + BM : ge;
+  }
+  tg.n0 = (int64_t)nt * BN;
+  return tg;
+}
+
+// Per-thread load plan of one tile: uniform bases and per-lane offsets.
+struct LoadPlan {
+  const uint8_t *a_base, *b_base, *sa_base, *sb_base;
+  uint32_t a_off[LOADS], b_off[LOADS];
+  uint32_t sa_off, sb_off;
+};
+
+__device__ __forceinline__ LoadPlan make_plan(const GemmArgs& p, const TileGeom& tg, int w, int lane) {
+  LoadPlan lp;
+  lp.a_base = uniform_ptr(p.a + tg.row0 * p.lda);
+  lp.b_base = uniform_ptr(p.b + (int64_t)tg.g * p.b_stride + tg.n0 * p.lda);
+  lp.sa_base = uniform_ptr(p.sfa + tg.row0 * p.ldsf);
+  lp.sb_base = uniform_ptr(p.sfb + (int64_t)tg.g * p.sfb_stride + tg.n0 * p.ldsf);
+  const int a_rows = (int)(tg.row_end - tg.row0);
+  const int b_rows = (int)(p.n - tg.n0 < BN ? p.n - tg.n0 : BN);
+  // load i of wave w fills LDS rows [(i*4 + w) * 8, +8); lane j -> row + j/8,
+  // physical chunk j % 8, logical chunk (j % 8) ^ swz(row).  Rows past the
+  // tile end re-read a valid row (their results are never stored).
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    int row = (i * WAVES + w) * 8 + (lane >> 3);
+    int c = (lane & 7) ^ swz(row);
+    int ra = row < a_rows ? row : a_rows - 1;
+    int rb = row < b_rows ? row : b_rows - 1;
+    lp.a_off[i] = (uint32_t)(ra * p.lda + c * 16);
+    lp.b_off[i] = (uint32_t)(rb * p.lda + c * 16);
+  }
+  // scales: wave w loads rows [64w, 64w + 64) of A and of B
+  int row = w * 64 + lane;
+  int ra = row < a_rows ? row : a_rows - 1;
+  int rb = row < b_rows ? row : b_rows - 1;
+  lp.sa_off = (uint32_t)(ra * p.ldsf);
+  lp.sb_off = (uint32_t)(rb * p.ldsf);
+  return lp;
+}
+
+// Issues K step k of a tile into LDS stage `st`: Cfg<FMT>::OPS operations.
+template <int FMT>
+__device__ __forceinline__ void issue(const LoadPlan& lp, int k, const uint8_t* st, int w) {
+  using C = Cfg<FMT>;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
+  const uint32_t la = base + w * 1024;
+  const uint32_t lb = la + C::A_BYTES;
+  const uint8_t* ak = lp.a_base + k * SROW;
+  const uint8_t* bk = lp.b_base + k * SROW;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) dma16(ak, lp.a_off[i], la + i * WAVES * 1024);
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) dma16(bk, lp.b_off[i], lb + i * WAVES * 1024);
+  // scale planes: dword plane h of row r at plane h * rows + r
+  const uint32_t lsa = base + C::A_BYTES + C::B_BYTES + w * 256;
+  const uint32_t lsb = lsa + BM * C::SB;
+#pragma unroll
+  for (int h = 0; h < C::PLANES; ++h) {
+    dma4(lp.sa_base + k * C::SB + 4 * h, lp.sa_off, lsa + h * BM * 4);
+    dma4(lp.sb_base + k * C::SB + 4 * h, lp.sb_off, lsb + h * BN * 4);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence: the kernel's own waits order the
+// LDS traffic (all fragment reads are consumed by matrix instructions before
+// a wave reaches the barrier), and a fence would also wait for the epilogue
+// stores.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
+  using C = Cfg<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TileTable tt;
 
-  const int G = p.num_groups;
+  const int G0 = p.num_groups;
   const int NT = (int)((p.n + BN - 1) / BN);
   const int mt_per = p.form == kUniform ? (int)((p.slot_rows + BM - 1) / BM) : 0;
   int total_gm;
-  if (p.form == kUniform) total_gm = G * mt_per;
+  if (p.form == kUniform) total_gm = G0 * mt_per;
   else total_gm = build_tile_table(p, BM, tt);
   const int total = total_gm * NT;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int q = lane >> 4, r16 = lane & 15;
-  const int wm = w >> 1, wn = w & 1;
-  const int nk = (int)(p.lda / 128);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;                        // 2 x 2 wave grid
+  const int h = lane >> 5, r32 = lane & 31;
+  const int nk = (int)(p.lda / SROW);
 
-  // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs,
-  // so workgroup b runs on XCD b % 8.  Rounds of gridDim tiles; inside a
-  // round XCD x owns a contiguous run of tiles.
+  // XCD-aware order: workgroup b runs on XCD b % 8; inside a round of
+  // gridDim tiles XCD x owns a contiguous run of tiles.
   const int nxcd = gridDim.x >= 8 ? 8 : 1;
   const int per_xcd = gridDim.x / nxcd;
   const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
-  const bool slot_ok = (int)blockIdx.x < per_xcd * nxcd;
+  const int stride = per_xcd * nxcd;
+  if ((int)blockIdx.x >= stride) return;
+  int t = slot;
+  if (t >= total) return;
 
-  for (int round = 0; slot_ok; ++round) {
-    const int t = round * (per_xcd * nxcd) + slot;
-    if (t >= total) break;
-    // tile t -> (group m-tile gm, n tile nt): blocks of 4 m-tiles x all n-tiles,
-    // walked n-major inside the block so 32 consecutive tiles = 4 m x 8 n.
-    const int blk = t / (4 * NT);
-    const int rem = t - blk * 4 * NT;
-    const int mrem = total_gm - blk * 4;
-    const int mb = mrem < 4 ? mrem : 4;
-    const int nt = rem / mb;
-    const int gm = blk * 4 + (rem - nt * mb);
+  TileGeom tg = tile_geom(p, tt, total_gm, NT, mt_per, t);
+  LoadPlan lp = make_plan(p, tg, w, lane);
+  int stage = 0;
+  issue<FMT>(lp, 0, smem, w);
+  wait_vm<0>();
+  bar();
 
-    int g;
-    int64_t row0, row_end;
-    if (p.form == kUniform) {
-      g = gm / mt_per;
-      int mt = gm - g * mt_per;
-      int64_t gs = (int64_t)g * p.slot_rows;
-      row0 = gs + (int64_t)mt * BM;
-      row_end = row0 + BM < gs + p.slot_rows ? row0 + BM : gs + p.slot_rows;
-    } else {
-      g = tile_group(tt, G, gm);
-      int mt = gm - (g > 0 ? tt.mt_prefix[g - 1] : 0);
-      row0 = (int64_t)tt.start[g] + (int64_t)mt * BM;
-      int64_t ge = (int64_t)tt.start[g] + tt.count[g];
-      row_end = row0 + BM < ge ? row0 + BM : ge;
-    }
-    const int64_t n0 = (int64_t)nt * BN;
+  v16f acc[4][4];
 
-    // ---- per-thread sources for the direct-to-LDS loads, as 32-bit offsets
-    // from uniform tile bases.  Load i of wave w fills LDS rows
-    // [(i*4 + w) * 8, +8); lane j -> row + j/8, physical chunk j % 8, logical
-    // chunk (j % 8) ^ swz(row).  Rows past the tile end re-read a valid row.
-    const uint8_t* a_base = uniform_ptr(p.a + row0 * p.lda);
-    const uint8_t* b_base = uniform_ptr(p.b + (int64_t)g * p.b_stride + n0 * p.lda);
-    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
-    const int64_t a_rows = row_end - row0;
-    const int64_t b_rows = p.n - n0 < BN ? p.n - n0 : BN;
+  // one K step on stage `cur`: read fragments of a half step, multiply, twice
+  auto step = [&](const uint8_t* cur) {
+    const uint8_t* la = cur;
+    const uint8_t* lb = cur + C::A_BYTES;
+    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES;
+    const uint8_t* lsb = lsa + BM * C::SB;
+    uint32_t asc[4][C::PLANES], bsc[4][C::PLANES];
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-      int row = (i * 4 + w) * 8 + (lane >> 3);
-      int c = (lane & 7) ^ swz(row);
-      int rr = row < a_rows ? row : (int)a_rows - 1;
-      a_off[i] = (uint32_t)(rr * p.lda + c * 16);
-    }
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * WT + i * 32 + r32, rb = wn * WT + i * 32 + r32;
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-      int row = (i * 4 + w) * 8 + (lane >> 3);
-      int c = (lane & 7) ^ swz(row);
-      int rr = row < b_rows ? row : (int)b_rows - 1;
-      b_off[i] = (uint32_t)(rr * p.lda + c * 16);
-    }
-    // scales: dword plane h of row r sits at plane h * rows + r; wave w loads
-    // rows [64w, 64w + 64) of each plane (waves past the tile skip).
-    const uint8_t* sa_base = uniform_ptr(p.sfa + row0 * p.ldsf);
-    const uint8_t* sb_base = uniform_ptr(p.sfb + (int64_t)g * p.sfb_stride + n0 * p.ldsf);
-    uint32_t sa_off, sb_off;
-    {
-      int row = w * 64 + lane;
-      int ra = row < a_rows ? row : (int)a_rows - 1;
-      int rb = row < b_rows ? row : (int)b_rows - 1;
-      sa_off = (uint32_t)(ra * p.ldsf);
-      sb_off = (uint32_t)(rb * p.ldsf);
-    }
-
-    // sbase operands must be wave-uniform: every address above is built from
-    // uniform values, and the LDS bases go through readfirstlane.
-    auto issue = [&](int ks, const uint8_t* st) {
-      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(st) + w * 1024);
-      const uint32_t lb = la + C::A_BYTES;
-      const uint32_t lsa = __builtin_amdgcn_readfirstlane(lds_addr(st) + C::A_BYTES + C::B_BYTES + w * 256);
-      const uint32_t lsb = lsa + C::SA_BYTES;
-      const uint8_t* ak = a_base + ks * 128;
-      const uint8_t* bk = b_base + ks * 128;
-#pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i) dma16(ak, a_off[i], la + i * 4096);
-#pragma unroll
-      for (int i = 0; i < C::B_LOADS; ++i) dma16(bk, b_off[i], lb + i * 4096);
-      const uint8_t* sak = sa_base + ks * C::SB;
-      const uint8_t* sbk = sb_base + ks * C::SB;
-#pragma unroll
-      for (int h = 0; h < C::PLANES; ++h) {
-        if (w * 64 < BM) dma4(sak + 4 * h, sa_off, lsa + h * BM * 4);
-        if (w * 64 < BN) dma4(sbk + 4 * h, sb_off, lsb + h * BN * 4);
+      for (int q = 0; q < C::PLANES; ++q) {
+        asc[i][q] = lds_read4(lsa + q * BM * 4 + ra * 4);
+        bsc[i][q] = lds_read4(lsb + q * BN * 4 + rb * 4);
       }
-    };
-
-    v4f acc[C::FM][C::FN];
+    }
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int half = 0; half < 2; ++half) {
+      // chunks 4*half + h and 4*half + 2 + h of every fragment row
+      uint4 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    issue(0, smem);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int ks = 0; ks < nk; ++ks) {
-      const uint8_t* cur = smem + (ks & 1) * C::STAGE;
-      // 1. the next K step's loads go out first and fly during this step
-      if (ks + 1 < nk) issue(ks + 1, smem + ((ks + 1) & 1) * C::STAGE);
-      const uint8_t* la = cur;
-      const uint8_t* lb = cur + C::A_BYTES;
-      const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES;
-      const uint8_t* lsb = lsa + C::SA_BYTES;
-
-      // 2. the wave's B fragments (weights, src0) stay in registers
-      uint4 blo[C::FN], bhi[C::FN];
-      uint32_t bsc[C::FN][C::PLANES];
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        int row = wn * (BN / 2) + j * 16 + r16;
-        const uint8_t* rp = lb + row * 128;
-        int s = swz(row);
-        blo[j] = lds_read16(rp + ((q ^ s) << 4));
-        bhi[j] = lds_read16(rp + (((q + 4) ^ s) << 4));
-#pragma unroll
-        for (int h = 0; h < C::PLANES; ++h)
-          bsc[j][h] = (*reinterpret_cast<const uint32_t*>(lsb + h * BN * 4 + row * 4) >> (8 * q)) & 0xFFu;
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * WT + i * 32 + r32, rb = wn * WT + i * 32 + r32;
+        const int sa = swz(ra), sb = swz(rb);
+        a0[i] = lds_read16(la + ra * SROW + (((4 * half + h) ^ sa) << 4));
+        a1[i] = lds_read16(la + ra * SROW + (((4 * half + 2 + h) ^ sa) << 4));
+        b0[i] = lds_read16(lb + rb * SROW + (((4 * half + h) ^ sb) << 4));
+        b1[i] = lds_read16(lb + rb * SROW + (((4 * half + 2 + h) ^ sb) << 4));
       }
-      // 3. A fragments stream through, each against every B fragment
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        int row = wm * (BM / 2) + i * 16 + r16;
-        const uint8_t* rp = la + row * 128;
-        int s = swz(row);
-        uint4 alo = lds_read16(rp + ((q ^ s) << 4));
-        uint4 ahi = lds_read16(rp + (((q + 4) ^ s) << 4));
-        uint32_t asc[C::PLANES];
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int h = 0; h < C::PLANES; ++h)
-          asc[h] = (*reinterpret_cast<const uint32_t*>(lsa + h * BM * 4 + row * 4) >> (8 * q)) & 0xFFu;
-        if (FMT == 0) {
-          v8i af = v8i{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            v8i bf = v8i{(int)blo[j].x, (int)blo[j].y, (int)blo[j].z, (int)blo[j].w,
-                         (int)bhi[j].x, (int)bhi[j].y, (int)bhi[j].z, (int)bhi[j].w};
-            acc[i][j] = mfma_scaled<0>(bf, af, acc[i][j], (int)bsc[j][0], (int)asc[0]);
-          }
-        } else {
-          v8i af0 = v8i{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, 0, 0, 0, 0};
-          v8i af1 = v8i{(int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w, 0, 0, 0, 0};
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            v8i bf0 = v8i{(int)blo[j].x, (int)blo[j].y, (int)blo[j].z, (int)blo[j].w, 0, 0, 0, 0};
-            v8i bf1 = v8i{(int)bhi[j].x, (int)bhi[j].y, (int)bhi[j].z, (int)bhi[j].w, 0, 0, 0, 0};
-            acc[i][j] = mfma_scaled<4>(bf0, af0, acc[i][j], (int)bsc[j][0], (int)asc[0]);
-            acc[i][j] = mfma_scaled<4>(bf1, af1, acc[i][j], (int)bsc[j][C::PLANES - 1], (int)asc[C::PLANES - 1]);
+        for (int j = 0; j < 4; ++j) {
+          if (FMT == 0) {
+            // FP8 step `half` covers blocks 2*half + {0,1}: lane group h
+            // carries block 2*half + h (byte of the single plane)
+            const int sh = 8 * (2 * half + h);
+            v8i af = v8i{(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
+                         (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
+            v8i bf = v8i{(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w,
+                         (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
+            acc[i][j] = mfma32<0>(bf, af, acc[i][j], (int)((bsc[j][0] >> sh) & 0xFFu),
+                                  (int)((asc[i][0] >> sh) & 0xFFu));
+          } else {
+            // FP4 steps 2*half (chunk 4*half + h) and 2*half + 1 (chunk
+            // 4*half + 2 + h); step v, lane group h: block 2v + h =
+            // plane v/2 = half, byte 2(v%2) + h
+            const int sh0 = 8 * h, sh1 = 8 * (2 + h);
+            v8i af0 = v8i{(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w, 0, 0, 0, 0};
+            v8i af1 = v8i{(int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w, 0, 0, 0, 0};
+            v8i bf0 = v8i{(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w, 0, 0, 0, 0};
+            v8i bf1 = v8i{(int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w, 0, 0, 0, 0};
+            const uint32_t bs = bsc[j][C::PLANES - 1 - (1 - half) * (C::PLANES - 1)];
+            const uint32_t as = asc[i][C::PLANES - 1 - (1 - half) * (C::PLANES - 1)];
+            acc[i][j] = mfma32<4>(bf0, af0, acc[i][j], (int)((bs >> sh0) & 0xFFu), (int)((as >> sh0) & 0xFFu));
+            acc[i][j] = mfma32<4>(bf1, af1, acc[i][j], (int)((bs >> sh1) & 0xFFu), (int)((as >> sh1) & 0xFFu));
           }
         }
       }
-      // 4. stage hand-over: keep every instruction of this step above the wait
+    }
+  };
+
+  bool prior_stores = false;
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // step 0: its stage is visible.  The prefetch of step 1 is issued after
+    // the previous tile's stores, so waiting for it also drains them.
+    for (int k = 0; k + 1 < nk; ++k) {
+      issue<FMT>(lp, k + 1, smem + (stage ^ 1) * C::STAGE, w);
+      step(smem + stage * C::STAGE);
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      wait_vm<0>();
+      bar();
+      stage ^= 1;
     }
+    // last step: prefetch the next tile's first step
+    const int t_next = t + stride;
+    const bool has_next = t_next < total;
+    TileGeom tg_next = tg;
+    LoadPlan lp_next = lp;
+    if (has_next) {
+      tg_next = tile_geom(p, tt, total_gm, NT, mt_per, t_next);
+      lp_next = make_plan(p, tg_next, w, lane);
+      issue<FMT>(lp_next, 0, smem + (stage ^ 1) * C::STAGE, w);
+    }
+    step(smem + stage * C::STAGE);
+    bar();                 // stage `stage` free; the next tile's step 0 is in flight
+    stage ^= 1;
 
-    // ---- epilogue: lane holds out[m = row][n = 4q + r] of each fragment
-    const uint16_t* bias = p.bias ? p.bias + (int64_t)g * p.n : nullptr;
+    // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
+    // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
+    // in register 4b + r, i.e. out[m = l%32][n = 8b + 4(l/32) + r].  Lanes l
+    // and l^32 swap one 4-column quad so each lane owns 8 consecutive
+    // columns: lane group 0 stores columns 8b..8b+7 for b = 0, 2 and lane
+    // group 1 for b = 1, 3.
+    const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tg.row0 * p.n));
+    const uint32_t obytes = __builtin_amdgcn_readfirstlane((uint32_t)((tg.row_end - tg.row0) * p.n * 2));
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
+    const uint16_t* bias = p.bias ? p.bias + (int64_t)tg.g * p.n : nullptr;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int64_t m = row0 + wm * (BM / 2) + i * 16 + r16;
-      if (m < row_end) {
+    for (int j = 0; j < 4; ++j) {
+      v4f bq[4];
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int64_t n = n0 + wn * (BN / 2) + j * 16 + 4 * q;
-          if (n < p.n) store_bf16x4(p.out + m * p.n + n, acc[i][j], bias ? bias + n : nullptr);
+      for (int b = 0; b < 4; ++b) {
+        const int64_t n = tg.n0 + wn * WT + j * 32 + 8 * b + 4 * h;
+        bq[b] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (bias != nullptr && n < p.n) {
+          uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+          bq[b] = v4f{bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t mr = wm * WT + i * 32 + r32;             // row within the tile
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          pk[b][0] = pack_bf16x2(acc[i][j][4 * b] + bq[b][0], acc[i][j][4 * b + 1] + bq[b][1]);
+          pk[b][1] = pack_bf16x2(acc[i][j][4 * b + 2] + bq[b][2], acc[i][j][4 * b + 3] + bq[b][3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
+          const int bl = 2 * e, bh = 2 * e + 1;
+          // group 0 sends its b = 2e+1 quad and receives the partner's b = 2e
+          // quad; group 1 the other way round
+          uint32_t s0 = h == 0 ? pk[bh][0] : pk[bl][0];
+          uint32_t s1 = h == 0 ? pk[bh][1] : pk[bl][1];
+          uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64);
+          uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+          v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
+          const int64_t n = tg.n0 + wn * WT + j * 32 + 8 * (h == 0 ? bl : bh);
+          const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
         }
       }
     }
+    if (!has_next) break;
+    // the next tile's step 0 was issued before these kStores stores
+    wait_vm<kStores>();
+    bar();
+    t = t_next;
+    tg = tg_next;
+    lp = lp_next;
+    prior_stores = true;
   }
+  (void)prior_stores;
 }
 
-template <int FMT, int BM, int BN>
+template <int FMT>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
-  using C = TiledCfg<FMT, BM, BN>;
-  const size_t smem = 2 * (size_t)C::STAGE;
+  using C = Cfg<FMT>;
+  const int smem = 2 * C::STAGE;
   static bool attr_set = false;   // per process; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, BM, BN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -308,7 +432,7 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (tiles < grid) grid = tiles;
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((mx_gemm_tiled<FMT, BM, BN>), dim3((unsigned)grid), dim3(kThreads), smem, s, p);
+  hipLaunchKernelGGL((mx_gemm_tiled<FMT>), dim3((unsigned)grid), dim3(THREADS), smem, s, p);
   return hipGetLastError();
 }
 
@@ -320,12 +444,13 @@ bool tiled_supported(const GemmArgs& p) {
   if (p.k % step != 0) return false;
   if ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 3) return false;
   if (p.lda * 256 >= (int64_t)1 << 31) return false;
+  if (p.n * 256 * 2 > 0x7FFFFFFFLL) return false;   // 32-bit output offsets below the drop marker
   return true;
 }
 
 hipError_t launch_gemm_tiled(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
-  if (p.mode == kMXFP8) return launch_tiled_cfg<0, 256, 256>(s, p, dev);
-  return launch_tiled_cfg<4, 256, 256>(s, p, dev);
+  if (p.mode == kMXFP8) return launch_tiled_cfg<0>(s, p, dev);
+  return launch_tiled_cfg<4>(s, p, dev);
 }
 
 }  // namespace hq
