@@ -11,19 +11,24 @@
 //     elements).  A 128 x 128 wave tile keeps the LDS fragment traffic at
 //     1/128 byte per FLOP, which the LDS can serve at the matrix-core rate.
 //   * A stage holds 128 bytes of every row of the A and B tiles: 128 FP8
-//     elements (two MFMA steps of 64) or 256 FP4 elements (four steps).  In
+//     elements (two MFMA sub-steps of 64) or 256 FP4 elements (four).  In
 //     both formats a lane reads 16-byte chunks h, 2+h, 4+h, 6+h of its
 //     fragment row (h = lane / 32): FP8 pairs them as (h, 2+h), (4+h, 6+h);
-//     FP4 uses each chunk as one step.
-//   * Global -> LDS with 16-byte direct-to-LDS loads into an XOR-swizzled
-//     layout; a wave's load fills 1 KB = 8 rows, lane j fetching the chunk
-//     that belongs at slot j.
-//   * Two LDS stages: the loads of step k+1 fly during step k, and the loads
-//     of the first step of the workgroup's next tile fly during the last step
-//     of the current tile, ahead of its epilogue stores.  Vector-memory
-//     operations retire in issue order, so every wait names how many later
-//     operations may stay in flight and the stores drain under the next
-//     tile's first step.
+//     FP4 uses each chunk as one sub-step.
+//   * Global -> LDS with 16-byte direct-to-LDS buffer loads into an
+//     XOR-swizzled layout; a wave's load fills 1 KB = 8 rows, lane j fetching
+//     the chunk that belongs at slot j.  The buffer descriptor of a tile ends
+//     at the end of the operand's allocation, so rows past it are dropped by
+//     the range check instead of being clamped; rows past a tile's own end
+//     (a group's last partial tile) read neighbouring valid rows whose
+//     results are never stored.  Per-lane load offsets are therefore the same
+//     for every tile and K step.
+//   * Two LDS stages: the loads of step k+1 fly during step k.  At a tile
+//     boundary the loads of the next tile's first two steps are issued before
+//     the epilogue stores, so the stores drain under the next tile's first
+//     two steps.  Vector-memory operations retire in issue order; every wait
+//     names how many later operations may stay in flight, which is correct
+//     whenever at least that many were issued after the awaited one.
 //   * Persistent grid, one workgroup per compute unit.  Tiles are ordered so
 //     that the 32 consecutive tiles one XCD (one L2) runs side by side cover
 //     4 row tiles x 8 column tiles.
@@ -47,28 +52,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_cptr_t)p;
 }
 
-// A pointer the compiler cannot prove uniform (it came through LDS), made
-// uniform explicitly; the value is the same in every lane.
+__device__ __forceinline__ uint32_t ufirst(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t ufirst64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)(((uint64_t)ufirst((uint32_t)(u >> 32)) << 32) | ufirst((uint32_t)u));
+}
+// A pointer the compiler cannot prove uniform, made uniform explicitly; the
+// value is the same in every lane.
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  uint64_t v = (uint64_t)(uintptr_t)p;
-  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return (const uint8_t*)(uintptr_t)ufirst64((int64_t)(uintptr_t)p);
 }
 
-// Direct-to-LDS loads: every lane fetches `size` bytes from sbase + voff and
-// the wave's 64 results land contiguously at LDS address m0 (lane j at
-// m0 + j * size).  Issued as inline assembly so that the compiler inserts no
-// alias waits of its own: the kernel orders these writes explicitly (a wait
-// on the vector-memory counter, then a workgroup barrier, before a stage is
-// read; a barrier after the last read of a stage before it is refilled).  m0
-// is set inside each statement; nothing else in the kernel uses it.
-__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+// Raw buffer descriptor over [base, base + bytes); `bytes` saturates at the
+// 32-bit record limit (a tile never reads that far).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// Direct-to-LDS buffer loads: every lane fetches `size` bytes at byte offset
+// voff of the buffer (nothing if out of range) and the wave's 64 results land
+// contiguously at LDS address m0 (lane j at m0 + j * size).  Issued as inline
+// assembly so that the compiler inserts no alias waits of its own: the kernel
+// orders these writes explicitly (a wait on the vector-memory counter, then a
+// workgroup barrier, before a stage is read; a barrier after the last read of
+// a stage before it is refilled).  m0 is set inside each statement; nothing
+// else in the kernel uses it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
                "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
                "s"(lds) : "memory");
 }
 
@@ -102,14 +117,17 @@ struct Cfg {
   static constexpr int OPS = 2 * LOADS + 2 * PLANES;  // vector-memory ops per stage per thread
 };
 
-// Where a tile sits: group, first row, row end and first column.
-struct TileGeom {
+// Where a tile sits (uniform): group, first row, row end, first column, and
+// the byte bases / extents of its operands.
+struct Tile {
   int g;
   int64_t row0, row_end, n0;
+  const uint8_t *a, *b, *sa, *sb;
+  int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
 };
 
-__device__ __forceinline__ TileGeom tile_geom(const GemmArgs& p, const TileTable& tt, int total_gm,
-                                              int NT, int mt_per, int t) {
+__device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TileTable& tt, int total_gm,
+                                          int NT, int mt_per, int t) {
   // blocks of 4 m-tiles x all n-tiles, walked n-major inside the block so 32
   // consecutive tiles = 4 m x 8 n
   const int blk = t / (4 * NT);
@@ -118,80 +136,84 @@ __device__ __forceinline__ TileGeom tile_geom(const GemmArgs& p, const TileTable
   const int mb = mrem < 4 ? mrem : 4;
   const int nt = rem / mb;
   const int gm = blk * 4 + (rem - nt * mb);
-  TileGeom tg;
+  int g;
+  int64_t row0, row_end;
   if (p.form == kUniform) {
-    tg.g = gm / mt_per;
-    int mt = gm - tg.g * mt_per;
-    int64_t gs = (int64_t)tg.g * p.slot_rows;
-    tg.row0 = gs + (int64_t)mt * BM;
-    tg.row_end = tg.row0 + BM < gs + p.slot_rows ? tg.row0 + BM : gs + p.slot_rows;
+    g = gm / mt_per;
+    const int mt = gm - g * mt_per;
+    const int64_t gs = (int64_t)g * p.slot_rows;
+    row0 = gs + (int64_t)mt * BM;
+    row_end = row0 + BM < gs + p.slot_rows ? row0 + BM : gs + p.slot_rows;
   } else {
-    tg.g = tile_group(tt, p.num_groups, gm);
-    int mt = gm - (tg.g > 0 ? tt.mt_prefix[tg.g - 1] : 0);
-    tg.row0 = (int64_t)tt.start[tg.g] + (int64_t)mt * BM;
-    int64_t ge = (int64_t)tt.start[tg.g] + tt.count[tg.g];
-    tg.row_end = tg.row0 + BM < ge ? tg.row0 + BM : ge;
+    g = tile_group(tt, p.num_groups, gm);
+    const int mt = gm - (g > 0 ? tt.mt_prefix[g - 1] : 0);
+    row0 = (int64_t)tt.start[g] + (int64_t)mt * BM;
+    const int64_t ge = (int64_t)tt.start[g] + tt.count[g];
+    row_end = row0 + BM < ge ? row0 + BM : ge;
   }
-  tg.n0 = (int64_t)nt * BN;
-  return tg;
+  Tile tl;
+  tl.g = (int)ufirst((uint32_t)g);
+  tl.row0 = ufirst64(row0);
+  tl.row_end = ufirst64(row_end);
+  tl.n0 = (int64_t)nt * BN;
+  const int64_t brow0 = (int64_t)tl.g * p.n + tl.n0;          // first weight row
+  const int64_t brows = (int64_t)p.num_groups * p.n;
+  tl.a = uniform_ptr(p.a + tl.row0 * p.lda);
+  tl.b = uniform_ptr(p.b + brow0 * p.lda);
+  tl.sa = uniform_ptr(p.sfa + tl.row0 * p.ldsf);
+  tl.sb = uniform_ptr(p.sfb + brow0 * p.ldsf);
+  tl.a_bytes = (p.m_rows - tl.row0) * p.lda;
+  tl.b_bytes = (brows - brow0) * p.lda;
+  tl.sa_bytes = (p.m_rows - tl.row0) * p.ldsf;
+  tl.sb_bytes = (brows - brow0) * p.ldsf;
+  return tl;
 }
 
-// Per-thread load plan of one tile: uniform bases and per-lane offsets.
-struct LoadPlan {
-  const uint8_t *a_base, *b_base, *sa_base, *sb_base;
-  uint32_t a_off[LOADS], b_off[LOADS];
-  uint32_t sa_off, sb_off;
+// Per-lane load offsets, the same for every tile and step.  Load i of wave w
+// fills LDS rows [(i*4 + w) * 8, +8) of the A and of the B tile; lane j ->
+// row + j/8, physical chunk j % 8, logical chunk (j % 8) ^ swz(row).  Scale
+// dwords: wave w loads rows [64w, 64w + 64).
+struct LoadOffsets {
+  uint32_t tile[LOADS];
+  uint32_t scale;
 };
 
-__device__ __forceinline__ LoadPlan make_plan(const GemmArgs& p, const TileGeom& tg, int w, int lane) {
-  LoadPlan lp;
-  lp.a_base = uniform_ptr(p.a + tg.row0 * p.lda);
-  lp.b_base = uniform_ptr(p.b + (int64_t)tg.g * p.b_stride + tg.n0 * p.lda);
-  lp.sa_base = uniform_ptr(p.sfa + tg.row0 * p.ldsf);
-  lp.sb_base = uniform_ptr(p.sfb + (int64_t)tg.g * p.sfb_stride + tg.n0 * p.ldsf);
-  const int a_rows = (int)(tg.row_end - tg.row0);
-  const int b_rows = (int)(p.n - tg.n0 < BN ? p.n - tg.n0 : BN);
-  // load i of wave w fills LDS rows [(i*4 + w) * 8, +8); lane j -> row + j/8,
-  // physical chunk j % 8, logical chunk (j % 8) ^ swz(row).  Rows past the
-  // tile end re-read a valid row (their results are never stored).
+__device__ __forceinline__ LoadOffsets make_offsets(const GemmArgs& p, int w, int lane) {
+  LoadOffsets o;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    int row = (i * WAVES + w) * 8 + (lane >> 3);
-    int c = (lane & 7) ^ swz(row);
-    int ra = row < a_rows ? row : a_rows - 1;
-    int rb = row < b_rows ? row : b_rows - 1;
-    lp.a_off[i] = (uint32_t)(ra * p.lda + c * 16);
-    lp.b_off[i] = (uint32_t)(rb * p.lda + c * 16);
+    const int row = (i * WAVES + w) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    o.tile[i] = (uint32_t)(row * p.lda + c * 16);
   }
-  // scales: wave w loads rows [64w, 64w + 64) of A and of B
-  int row = w * 64 + lane;
-  int ra = row < a_rows ? row : a_rows - 1;
-  int rb = row < b_rows ? row : b_rows - 1;
-  lp.sa_off = (uint32_t)(ra * p.ldsf);
-  lp.sb_off = (uint32_t)(rb * p.ldsf);
-  return lp;
+  o.scale = (uint32_t)((w * 64 + lane) * p.ldsf);
+  return o;
 }
 
-// Issues K step k of a tile into LDS stage `st`: Cfg<FMT>::OPS operations.
+// Issues K step k of tile `tl` into LDS stage `st`: Cfg<FMT>::OPS operations.
 template <int FMT>
-__device__ __forceinline__ void issue(const LoadPlan& lp, int k, const uint8_t* st, int w) {
+__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets& o, int k, const uint8_t* st,
+                                      int w) {
   using C = Cfg<FMT>;
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
+  const uint32_t base = ufirst(lds_addr(st));
   const uint32_t la = base + w * 1024;
   const uint32_t lb = la + C::A_BYTES;
-  const uint8_t* ak = lp.a_base + k * SROW;
-  const uint8_t* bk = lp.b_base + k * SROW;
+  const int64_t ka = (int64_t)k * SROW, ks = (int64_t)k * C::SB;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(tl.a + ka, tl.a_bytes - ka);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(tl.b + ka, tl.b_bytes - ka);
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) dma16(ak, lp.a_off[i], la + i * WAVES * 1024);
+  for (int i = 0; i < LOADS; ++i) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) dma16(bk, lp.b_off[i], lb + i * WAVES * 1024);
+  for (int i = 0; i < LOADS; ++i) dma16(rb, o.tile[i], lb + i * WAVES * 1024);
   // scale planes: dword plane h of row r at plane h * rows + r
   const uint32_t lsa = base + C::A_BYTES + C::B_BYTES + w * 256;
   const uint32_t lsb = lsa + BM * C::SB;
+  const __amdgpu_buffer_rsrc_t rsa = rsrc(tl.sa + ks, tl.sa_bytes - ks);
+  const __amdgpu_buffer_rsrc_t rsb = rsrc(tl.sb + ks, tl.sb_bytes - ks);
 #pragma unroll
   for (int h = 0; h < C::PLANES; ++h) {
-    dma4(lp.sa_base + k * C::SB + 4 * h, lp.sa_off, lsa + h * BM * 4);
-    dma4(lp.sb_base + k * C::SB + 4 * h, lp.sb_off, lsb + h * BN * 4);
+    dma4(rsa, o.scale + 4 * h, lsa + h * BM * 4);
+    dma4(rsb, o.scale + 4 * h, lsb + h * BN * 4);
   }
 }
 
@@ -210,8 +232,12 @@ __device__ __forceinline__ void bar() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Two FP32 values -> packed BF16 pair (low half = a), round to nearest even,
+// in one hardware conversion.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 template <int FMT>
@@ -229,7 +255,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   const int total = total_gm * NT;
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int w = ufirst(tid >> 6);                           // wave index (uniform)
   const int lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;                        // 2 x 2 wave grid
   const int h = lane >> 5, r32 = lane & 31;
@@ -245,76 +271,111 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   int t = slot;
   if (t >= total) return;
 
-  TileGeom tg = tile_geom(p, tt, total_gm, NT, mt_per, t);
-  LoadPlan lp = make_plan(p, tg, w, lane);
-  int stage = 0;
-  issue<FMT>(lp, 0, smem, w);
-  wait_vm<0>();
-  bar();
+  const LoadOffsets lo = make_offsets(p, w, lane);
+
+  // Fragment-read offsets.  Fragment row i of the wave tile is LDS row
+  // 128 wm + 32 i + r32 (A) / 128 wn + 32 i + r32 (B); its swizzle is
+  // s0 ^ 4 (i & 1) with s0 = swz(r32), so logical chunk c + h (c even) of
+  // row i sits at physical chunk ((c ^ 4 (i & 1)) | h) ^ s0.  xo[e] holds
+  // the lane's byte offset of logical chunk 2e + h in an i = 0 row; row i
+  // adds i * 4096 and flips e by 2 (i & 1).
+  const int s0 = swz(r32);
+  uint32_t xo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) xo[e] = (uint32_t)(r32 * SROW + ((((2 * e) | h) ^ s0) << 4));
+  auto rd16 = [&](const uint8_t* wbase, int i, int c) -> uint4 {
+    return lds_read16(wbase + i * 32 * SROW + xo[(c ^ (4 * (i & 1))) >> 1]);
+  };
 
   v16f acc[4][4];
 
-  // one K step on stage `cur`: read fragments of a half step, multiply, twice
+  // One K step on stage `cur`.  A step is SUB matrix-core sub-steps (two of
+  // K 64 for FP8, four of K 64 for FP4); sub-step v reads, per fragment row,
+  // chunks (4v + h, 4v + 2 + h) for FP8 and chunk 2v + h for FP4.  Fragment
+  // reads run one MFMA row ahead: while row i of sub-step v multiplies, the A
+  // fragment of row i + 1 and the B fragment j = i of sub-step v + 1 are read,
+  // so at most two B sets and two A fragments are live.  Scheduling fences
+  // keep the compiler from sinking the reads onto their first use.
+  constexpr int SUB = FMT == 0 ? 2 : 4;
+  struct Frag {
+    uint4 x, y;
+  };
+  auto rd = [&](const uint8_t* wbase, int i, int v) -> Frag {
+    Frag f;
+    if (FMT == 0) {
+      f.x = rd16(wbase, i, 4 * v);
+      f.y = rd16(wbase, i, 4 * v + 2);
+    } else {
+      f.x = rd16(wbase, i, 2 * v);
+      f.y = make_uint4(0, 0, 0, 0);
+    }
+    return f;
+  };
+  auto op = [](const Frag& f) -> v8i {
+    return FMT == 0 ? v8i{(int)f.x.x, (int)f.x.y, (int)f.x.z, (int)f.x.w,
+                          (int)f.y.x, (int)f.y.y, (int)f.y.z, (int)f.y.w}
+                    : v8i{(int)f.x.x, (int)f.x.y, (int)f.x.z, (int)f.x.w, 0, 0, 0, 0};
+  };
+  // scale byte of sub-step v for lane group h: FP8 block 2v + h of the one
+  // dword plane; FP4 block 2v + h = plane v / 2, byte 2 (v % 2) + h
+  auto sc = [&](const uint32_t (&d)[C::PLANES], int v) -> int {
+    const int plane = FMT == 0 ? 0 : v / 2;
+    const int byte = FMT == 0 ? 2 * v + h : 2 * (v % 2) + h;
+    return (int)((d[plane] >> (8 * byte)) & 0xFFu);
+  };
+
   auto step = [&](const uint8_t* cur) {
-    const uint8_t* la = cur;
-    const uint8_t* lb = cur + C::A_BYTES;
-    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES;
-    const uint8_t* lsb = lsa + BM * C::SB;
+    const uint8_t* la = cur + wm * WT * SROW;
+    const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
+    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
+    const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WT + r32) * 4;
+    Frag fa = rd(la, 0, 0);
+    Frag fb[4], fbn[4];
+    fb[0] = rd(lb, 0, 0);
     uint32_t asc[4][C::PLANES], bsc[4][C::PLANES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * WT + i * 32 + r32, rb = wn * WT + i * 32 + r32;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < C::PLANES; ++q) {
-        asc[i][q] = lds_read4(lsa + q * BM * 4 + ra * 4);
-        bsc[i][q] = lds_read4(lsb + q * BN * 4 + rb * 4);
-      }
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // chunks 4*half + h and 4*half + 2 + h of every fragment row
-      uint4 a0[4], a1[4], b0[4], b1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = wm * WT + i * 32 + r32, rb = wn * WT + i * 32 + r32;
-        const int sa = swz(ra), sb = swz(rb);
-        a0[i] = lds_read16(la + ra * SROW + (((4 * half + h) ^ sa) << 4));
-        a1[i] = lds_read16(la + ra * SROW + (((4 * half + 2 + h) ^ sa) << 4));
-        b0[i] = lds_read16(lb + rb * SROW + (((4 * half + h) ^ sb) << 4));
-        b1[i] = lds_read16(lb + rb * SROW + (((4 * half + 2 + h) ^ sb) << 4));
+        bsc[i][q] = lds_read4(lsb + q * BN * 4 + 32 * i * 4);
+        asc[i][q] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int j = 1; j < 4; ++j) fb[j] = rd(lb, j, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (FMT == 0) {
-            // FP8 step `half` covers blocks 2*half + {0,1}: lane group h
-            // carries block 2*half + h (byte of the single plane)
-            const int sh = 8 * (2 * half + h);
-            v8i af = v8i{(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
-                         (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
-            v8i bf = v8i{(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w,
-                         (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
-            acc[i][j] = mfma32<0>(bf, af, acc[i][j], (int)((bsc[j][0] >> sh) & 0xFFu),
-                                  (int)((asc[i][0] >> sh) & 0xFFu));
-          } else {
-            // FP4 steps 2*half (chunk 4*half + h) and 2*half + 1 (chunk
-            // 4*half + 2 + h); step v, lane group h: block 2v + h =
-            // plane v/2 = half, byte 2(v%2) + h
-            const int sh0 = 8 * h, sh1 = 8 * (2 + h);
-            v8i af0 = v8i{(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w, 0, 0, 0, 0};
-            v8i af1 = v8i{(int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w, 0, 0, 0, 0};
-            v8i bf0 = v8i{(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w, 0, 0, 0, 0};
-            v8i bf1 = v8i{(int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w, 0, 0, 0, 0};
-            const uint32_t bs = bsc[j][C::PLANES - 1 - (1 - half) * (C::PLANES - 1)];
-            const uint32_t as = asc[i][C::PLANES - 1 - (1 - half) * (C::PLANES - 1)];
-            acc[i][j] = mfma32<4>(bf0, af0, acc[i][j], (int)((bs >> sh0) & 0xFFu), (int)((as >> sh0) & 0xFFu));
-            acc[i][j] = mfma32<4>(bf1, af1, acc[i][j], (int)((bs >> sh1) & 0xFFu), (int)((as >> sh1) & 0xFFu));
-          }
-        }
+    for (int v = 0; v < SUB; ++v) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Frag fan = fa;
+        if (i < 3) fan = rd(la, i + 1, v);
+        else if (v + 1 < SUB) fan = rd(la, 0, v + 1);
+        if (v + 1 < SUB) fbn[i] = rd(lb, i, v + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const v8i af = op(fa);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma32<FMT>(op(fb[j]), af, acc[i][j], sc(bsc[j], v), sc(asc[i], v));
+        __builtin_amdgcn_sched_barrier(0);
+        fa = fan;
+      }
+      if (v + 1 < SUB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = fbn[j];
       }
     }
   };
+
+  Tile tl = make_tile(p, tt, total_gm, NT, mt_per, t);
+  int st = 0;                                   // stage of the current step
+  // first tile: steps 0 and 1 in flight, wait for step 0
+  issue<FMT>(tl, lo, 0, smem, w);
+  if (nk > 1) {
+    issue<FMT>(tl, lo, 1, smem + C::STAGE, w);
+    wait_vm<C::OPS>();
+  } else {
+    wait_vm<0>();
+  }
+  bar();
 
   bool prior_stores = false;
   while (true) {
@@ -325,29 +386,29 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // step 0: its stage is visible.  The prefetch of step 1 is issued after
-    // the previous tile's stores, so waiting for it also drains them.
+    // Steps 0 .. nk-2.  Step 1's loads were issued with step 0's, before the
+    // previous tile's stores; step k >= 1 issues step k + 1 into the stage
+    // step k - 1 used.
     for (int k = 0; k + 1 < nk; ++k) {
-      issue<FMT>(lp, k + 1, smem + (stage ^ 1) * C::STAGE, w);
-      step(smem + stage * C::STAGE);
+      if (k >= 1) issue<FMT>(tl, lo, k + 1, smem + (st ^ 1) * C::STAGE, w);
+      step(smem + st * C::STAGE);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<0>();
+      if (k == 0 && prior_stores) wait_vm<kStores>();   // stores stay in flight
+      else wait_vm<0>();
       bar();
-      stage ^= 1;
+      st ^= 1;
     }
-    // last step: prefetch the next tile's first step
+    // last step: the next tile's step 0 goes into the other stage
     const int t_next = t + stride;
     const bool has_next = t_next < total;
-    TileGeom tg_next = tg;
-    LoadPlan lp_next = lp;
+    Tile tn = tl;
     if (has_next) {
-      tg_next = tile_geom(p, tt, total_gm, NT, mt_per, t_next);
-      lp_next = make_plan(p, tg_next, w, lane);
-      issue<FMT>(lp_next, 0, smem + (stage ^ 1) * C::STAGE, w);
+      tn = make_tile(p, tt, total_gm, NT, mt_per, t_next);
+      issue<FMT>(tn, lo, 0, smem + (st ^ 1) * C::STAGE, w);
     }
-    step(smem + stage * C::STAGE);
-    bar();                 // stage `stage` free; the next tile's step 0 is in flight
-    stage ^= 1;
+    step(smem + st * C::STAGE);
+    bar();                            // stage `st` is free
+    if (has_next && nk > 1) issue<FMT>(tn, lo, 1, smem + st * C::STAGE, w);
 
     // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
     // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
@@ -355,17 +416,17 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     // and l^32 swap one 4-column quad so each lane owns 8 consecutive
     // columns: lane group 0 stores columns 8b..8b+7 for b = 0, 2 and lane
     // group 1 for b = 1, 3.
-    const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tg.row0 * p.n));
-    const uint32_t obytes = __builtin_amdgcn_readfirstlane((uint32_t)((tg.row_end - tg.row0) * p.n * 2));
+    const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tl.row0 * p.n));
+    const uint32_t obytes = ufirst((uint32_t)((tl.row_end - tl.row0) * p.n * 2));
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
-    const uint16_t* bias = p.bias ? p.bias + (int64_t)tg.g * p.n : nullptr;
+    const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v4f bq[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int64_t n = tg.n0 + wn * WT + j * 32 + 8 * b + 4 * h;
+        const int64_t n = tl.n0 + wn * WT + j * 32 + 8 * b + 4 * h;
         bq[b] = v4f{0.f, 0.f, 0.f, 0.f};
         if (bias != nullptr && n < p.n) {
           uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
@@ -386,28 +447,29 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
           const int bl = 2 * e, bh = 2 * e + 1;
           // group 0 sends its b = 2e+1 quad and receives the partner's b = 2e
           // quad; group 1 the other way round
-          uint32_t s0 = h == 0 ? pk[bh][0] : pk[bl][0];
-          uint32_t s1 = h == 0 ? pk[bh][1] : pk[bl][1];
-          uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64);
-          uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+          uint32_t s0w = h == 0 ? pk[bh][0] : pk[bl][0];
+          uint32_t s1w = h == 0 ? pk[bh][1] : pk[bl][1];
+          uint32_t r0 = (uint32_t)__shfl_xor((int)s0w, 32, 64);
+          uint32_t r1 = (uint32_t)__shfl_xor((int)s1w, 32, 64);
           typedef uint32_t v4u __attribute__((ext_vector_type(4)));
           v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
-          const int64_t n = tg.n0 + wn * WT + j * 32 + 8 * (h == 0 ? bl : bh);
+          const int64_t n = tl.n0 + wn * WT + j * 32 + 8 * (h == 0 ? bl : bh);
           const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
           __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
         }
       }
     }
     if (!has_next) break;
-    // the next tile's step 0 was issued before these kStores stores
-    wait_vm<kStores>();
+    // the next tile's step 0 was issued before its step 1 (nk > 1) and these
+    // kStores stores
+    if (nk > 1) wait_vm<C::OPS + kStores>();
+    else wait_vm<kStores>();
     bar();
     t = t_next;
-    tg = tg_next;
-    lp = lp_next;
+    tl = tn;
+    st ^= 1;
     prior_stores = true;
   }
-  (void)prior_stores;
 }
 
 template <int FMT>
