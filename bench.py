@@ -61,13 +61,21 @@ class Timer:
 
 
 def _traffic(kernel_key):
-    """HBM bytes per launch measured with counters (profiles/traffic.json),
-    or None when no measurement of the current kernel exists."""
+    """HBM bytes per launch measured with counters (profiles/traffic.json), or
+    None when there is no measurement or the kernel's sources changed since
+    the counters were taken (their SHA-256 no longer matches)."""
+    import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        return t.get(kernel_key)
-    except (OSError, ValueError):
+            rec = json.load(f).get(kernel_key)
+        if not rec:
+            return None
+        h = hashlib.sha256()
+        for name in rec["sources"]:
+            with open(os.path.join(ROOT, "fp4_gemm_moe_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        return int(rec["bytes"]) if h.hexdigest() == rec["sources_sha256"] else None
+    except (OSError, ValueError, KeyError, TypeError):
         return None
 
 
@@ -123,7 +131,7 @@ def run_moe(args, torch, hq, synth):
 
     ms_step = wall * 1e3 / args.steps
     flops = 2.0 * T * N * K
-    quant_bytes = T * K * (2 + 1 + 1 / 32)
+    quant_bytes = R * K * (2 + 1 + 1 / 32)     # the whole padded activation buffer
     swiglu_bytes = T * H * (4 + 1 + 1 / 32)
     gemm_ms = timer.mean_ms("gemm")
     quant_ms = timer.mean_ms("quant")
@@ -131,11 +139,13 @@ def run_moe(args, torch, hq, synth):
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     kernels = {
         "quant_mxfp8": {"ms": quant_ms, "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9,
-                        "frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                        "frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": _traffic("quant_mxfp8")},
         "grouped_gemm_mxfp8": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
                                "frac_mfma": gemm_tflops / PEAK_TFLOPS["mxfp8"]},
         "swiglu_quant_mxfp8": {"ms": sw_ms, "GB/s": swiglu_bytes / (sw_ms * 1e-3) / 1e9,
-                               "frac_hbm": swiglu_bytes / (sw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                               "frac_hbm": swiglu_bytes / (sw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "traffic": _traffic("swiglu_quant_mxfp8")},
     }
     cfg = {"workload": "moe_grouped_contiguous_mxfp8_E32_T65536_K4096_N3072_swiglu",
            "experts": E, "routed_rows": T, "padded_rows": R, "k": K, "n": N, "h": H,
@@ -217,7 +227,8 @@ def run_dense_fp4(args, torch, hq, synth):
     cfg = {"workload": f"dense_{mode}_M{m}_N{n}_K{k}", "m": m, "n": n, "k": k}
     roof = {"bound": "mfma" if m >= 512 else "hbm", "achieved": tf if m >= 512 else bytes_ / (ms * 1e-3) / 1e9,
             "peak": peak if m >= 512 else PEAK_HBM_GBS, "unit": "TFLOP/s" if m >= 512 else "GB/s",
-            "traffic": None}
+            "traffic": _traffic("dense_gemm_mxfp4")
+            if (mode, m, n, k) == ("mxfp4", 4096, 17408, 5120) else None}
     roof["frac"] = roof["achieved"] / roof["peak"]
     return tf, ms, cfg, roof, {"dense_gemm": {"ms": ms, "TFLOP/s": tf, "GB/s": bytes_ / (ms * 1e-3) / 1e9}}, None
 
