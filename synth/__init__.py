@@ -100,14 +100,20 @@ LARGE_NK = [(17408, 5120), (5120, 17408), (12288, 5120)]
 LARGE_M = [1, 16, 512, 4096]
 
 
+def dense_fp4_large_acts(n, k, m, seed=2):
+    """Activations N(0,1) [m, k] from SeedSequence(seed, spawn_key=(n, k, m))."""
+    return normal_bf16(np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(n, k, m))), (m, k))
+
+
+def dense_fp4_large_weights(n, k, seed=2):
+    """Weights N(0, 0.02) [n, k] from SeedSequence(seed, spawn_key=(n, k)):
+    every M of one (N, K) shares them."""
+    return normal_bf16(np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(n, k))), (n, k), 0.02)
+
+
 def dense_fp4_large(n, k, m, seed=2):
-    """Activations N(0,1) [m, k] and weights N(0, 0.02) [n, k].  The
-    activation stream is SeedSequence(seed, spawn_key=(n, k, m)); the weight
-    stream is SeedSequence(seed, spawn_key=(n, k)), so every M of one (N, K)
-    shares the same weights."""
-    a = normal_bf16(np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(n, k, m))), (m, k))
-    w = normal_bf16(np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(n, k))), (n, k), 0.02)
-    return {"a": a, "b": w}
+    """Activations [m, k] and weights [n, k] of one qualification shape."""
+    return {"a": dense_fp4_large_acts(n, k, m, seed), "b": dense_fp4_large_weights(n, k, seed)}
 
 
 def moe_contiguous(seed=3, E=32, tokens=16384, topk=4, K=4096, H=1536, align=128,
