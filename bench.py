@@ -15,6 +15,8 @@ dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
 and the oracle timed on a bounded sample on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload moe|dense_fp4|masked_fp4]
+    python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
+                                        # one JSON line per case
 """
 import argparse
 import json
@@ -267,12 +269,112 @@ def run_masked_fp4(args, torch, hq, synth):
     return tf, ms, cfg, roof, {"masked_gemm_mxfp4": {"ms": ms, "TFLOP/s": tf, "GB/s": gbs}}, None
 
 
+def _time_us(torch, fns, reps=15, per=20):
+    """Median over `reps` batches of the mean time per launch of a batch of
+    `per` launches (HIP events on the current stream); fns is cycled so that a
+    ring of buffers can be rotated through (cold-cache timing)."""
+    i = 0
+    for _ in range(10):
+        fns[i % len(fns)]()
+        i += 1
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(per):
+            fns[i % len(fns)]()
+            i += 1
+        e.record()
+        torch.cuda.synchronize()
+        res.append(s.elapsed_time(e) * 1e3 / per)
+    return float(np.median(res))
+
+
+def run_sweep(args, torch, hq, synth):
+    """The dense qualification grid (3 (N, K) x M in {1, 16, 512, 4096} x
+    {MXFP4, NVFP4}) and the standalone quantisation bandwidths, one JSON line
+    per case.  HBM-bound cases are timed warm and cold (a ring of >= 1 GB of
+    buffers rotated through, larger than the 256 MB Infinity Cache)."""
+    dev = torch.device("cuda:0")
+    ring_bytes = 1 << 30
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    for (n, k) in synth.LARGE_NK:
+        wbits = synth.dense_fp4_large_weights(n, k)
+        w = _dev_bf16(torch, wbits, dev)
+        for mode in ("mxfp4", "nvfp4"):
+            wq, wsf, gw = hq.quantize(w, mode)
+            wbytes = wq.numel() + wsf.numel()
+            copies = max(1, -(-ring_bytes // wbytes))
+            ring = [(wq.clone(), wsf.clone()) for _ in range(copies)]
+            for m in synth.LARGE_M:
+                x = _dev_bf16(torch, synth.dense_fp4_large_acts(n, k, m), dev)
+                aq, asf, ga = hq.quantize(x, mode)
+                alpha = (ga * gw) if mode == "nvfp4" else None
+                out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+                warm = _time_us(torch, [lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha)])
+                cold = None
+                if m <= 16:
+                    cold = _time_us(torch, [lambda q=q, s_=s_: hq.hq_dense_gemm(mode, aq, asf, q, s_, out,
+                                                                                   alpha=alpha)
+                                            for q, s_ in ring])
+                flops = 2.0 * m * n * k
+                gs = 16 if mode == "nvfp4" else 32
+                bytes_ = (m + n) * k * (0.5 + 1 / gs) + 2 * m * n
+                peak = PEAK_TFLOPS["nvfp4_bf16" if mode == "nvfp4" else mode]
+                t_ideal = max(flops / (peak * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e6
+                t = cold if cold is not None else warm
+                emit({"case": "dense_gemm", "mode": mode, "m": m, "n": n, "k": k,
+                      "us_warm": round(warm, 2), "us_cold": None if cold is None else round(cold, 2),
+                      "TFLOP/s": round(flops / (t * 1e-6) / 1e12, 1),
+                      "GB/s": round(bytes_ / (t * 1e-6) / 1e9, 1),
+                      "bound": "hbm" if bytes_ / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12) else "mfma",
+                      "t_ideal_us": round(t_ideal, 2), "roofline_frac": round(t_ideal / t, 3),
+                      "kernel": "direct" if m <= 16 else ("tiled" if mode != "nvfp4" else "direct_bf16")})
+                del x, aq, asf, out
+            del ring, wq, wsf
+        del w
+        torch.cuda.empty_cache()
+
+    quant_cases = [("mxfp8", 65536, 4096), ("mxfp4", 16384, 7168), ("mxfp4", 4096, 17408),
+                   ("nvfp4", 4096, 17408)]
+    rng = np.random.default_rng(5)
+    for mode, m, k in quant_cases:
+        x = _dev_bf16(torch, synth.normal_bf16(rng, (m, k)), dev)
+        copies = max(1, -(-ring_bytes // (2 * m * k)))
+        xs = [x] + [x.clone() for _ in range(copies - 1)]
+        q, sf, g = hq.quantize(x, mode)
+        gs = 16 if mode == "nvfp4" else 32
+        elem = 2 + (1 if mode == "mxfp8" else 0.5) + 1 / gs
+        variants = [("", None)] if mode != "nvfp4" else [(" amax", None), (" g supplied", g.clone())]
+        for tag, gin in variants:
+            def mk(xx, gin=gin):
+                if gin is None:
+                    return lambda: hq.hq_group_wise_quant(mode, xx, q, sf, g)
+                return lambda: hq.hq_group_wise_quant(mode, xx, q, sf, gin, hq.HQ_GS_INPUT)
+            warm = _time_us(torch, [mk(x)])
+            cold = _time_us(torch, [mk(xx) for xx in xs])
+            bytes_ = m * k * elem
+            extra = 2 * m * k if (mode == "nvfp4" and gin is None) else 0
+            emit({"case": "quant" + tag, "mode": mode, "m": m, "k": k,
+                  "us_warm": round(warm, 2), "us_cold": round(cold, 2),
+                  "GB/s": round(bytes_ / (cold * 1e-6) / 1e9, 1),
+                  "GB/s_incl_amax_pass": round((bytes_ + extra) / (cold * 1e-6) / 1e9, 1) if extra else None,
+                  "roofline_frac": round(bytes_ / (PEAK_HBM_GBS * 1e9) / (cold * 1e-6), 3)})
+        del x, xs, q, sf
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4", "sweep"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
@@ -306,6 +408,9 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {nbytes} bytes read and written once")
         del src, dst
+    if args.workload == "sweep":
+        run_sweep(args, torch, hq, synth)
+        return
     runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4}[args.workload]
     value, ms_step, cfg, roof, kernels, ctx = runner(args, torch, hq, synth)
     cpu = None

@@ -84,6 +84,58 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return e2m1_mag(u & 0x7fffffffu) | ((u >> 28) & 0x8u);
 }
 
+// Eight FP32 values of one MX block -> E4M3 codes (two dwords, element i in
+// byte i) or E2M1 nibbles (one dword, element i in nibble i), each value
+// divided by the block scale 2^(byte - 127), round to nearest even,
+// saturating -- with the gfx950 scaled conversions (two values per
+// instruction).  These use only the exponent of their scale operand and, for
+// power-of-two scales, give exactly e4m3_code / e2m1_code of x * 2^-(byte-127)
+// (checked on the device over every finite BF16 input and a range of scale
+// exponents), except that FP8 results beyond 448 become NaN rather than
+// saturate, hence the clamp to +-448 * scale first.  Blocks with byte < 64
+// (|x| < 2^-55) are first multiplied by 2^64, exactly, and converted with
+// byte + 64, so the scale operand stays a normal float.
+__device__ __forceinline__ float mx_hw_scale(uint32_t byte, float (&f)[8]) {
+  if (byte < 64u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] *= 18446744073709551616.0f;   // 2^64
+    byte += 64u;
+  }
+  return __uint_as_float(byte << 23);
+}
+
+__device__ __forceinline__ uint2 mx_fp8x8(const float (&x)[8], uint32_t byte) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = x[i];
+  const float sc = mx_hw_scale(byte, f);
+  const float lim = 448.0f * sc;
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, __builtin_amdgcn_fmed3f(f[0], -lim, lim),
+                                                __builtin_amdgcn_fmed3f(f[1], -lim, lim), sc, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, __builtin_amdgcn_fmed3f(f[2], -lim, lim),
+                                                __builtin_amdgcn_fmed3f(f[3], -lim, lim), sc, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, __builtin_amdgcn_fmed3f(f[4], -lim, lim),
+                                                __builtin_amdgcn_fmed3f(f[5], -lim, lim), sc, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, __builtin_amdgcn_fmed3f(f[6], -lim, lim),
+                                                __builtin_amdgcn_fmed3f(f[7], -lim, lim), sc, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+__device__ __forceinline__ uint32_t mx_fp4x8(const float (&x)[8], uint32_t byte) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = x[i];
+  const float sc = mx_hw_scale(byte, f);
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], sc, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], sc, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], sc, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], sc, 3);
+  return w;
+}
+
 // E4M3 / UE4M3 code -> FP32 value (exact).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   uint32_t e = (c >> 3) & 0xFu, m = c & 7u;

@@ -48,19 +48,10 @@ __device__ __forceinline__ void mx_emit(const Chunk8& c, uint32_t amax, int64_t 
                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
   constexpr int EMAX = MODE == kMXFP8 ? 8 : 2;
   uint32_t sb = mx_scale_byte<EMAX>(amax);
-  float inv = mx_inv_scale(sb);
   if (MODE == kMXFP8) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w0 |= e4m3_code(c.f[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w1 |= e4m3_code(c.f[4 + i] * inv) << (8 * i);
-    reinterpret_cast<uint2*>(q)[ci] = make_uint2(w0, w1);
+    reinterpret_cast<uint2*>(q)[ci] = mx_fp8x8(c.f, sb);
   } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_code(c.f[i] * inv) << (4 * i);
-    reinterpret_cast<uint32_t*>(q)[ci] = w;
+    reinterpret_cast<uint32_t*>(q)[ci] = mx_fp4x8(c.f, sb);
   }
   if ((ci & 3) == 0) sf[ci >> 2] = (uint8_t)sb;
 }
@@ -98,17 +89,38 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restr
 // bit pattern (order-preserving for non-negative floats), finalise in place.
 __global__ void nv_amax_zero(uint32_t* acc) { *acc = 0u; }
 
+// One atomic per workgroup: a wave reduction, then the first wave folds the
+// block's wave maxima.  The grid is a few workgroups per CU, each streaming
+// kUnroll independent 16-byte loads per thread per iteration.
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restrict__ x,
                                                            int64_t nchunks,
                                                            uint32_t* __restrict__ acc) {
+  __shared__ uint32_t wmax[kThreads / 64];
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t ci = (int64_t)blockIdx.x * kThreads + threadIdx.x; ci < nchunks; ci += stride) {
-    uint32_t a = abs_max_bits(unpack(load_nt(&x[ci])));
-    m = a > m ? a : m;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < nchunks;
+       base += stride * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t ci = base + u * stride;
+      v[u] = ci < nchunks ? load_nt(&x[ci]) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t a = abs_max_bits(unpack(v[u]));
+      m = a > m ? a : m;
+    }
   }
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(acc, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+    if (b != 0) atomicMax(acc, b);
+  }
 }
 
 __global__ void nv_gs_finalize(float* gs) {
@@ -185,7 +197,10 @@ hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, i
     if (!gs_input) {
       uint32_t* acc = reinterpret_cast<uint32_t*>(gs);
       hipLaunchKernelGGL(nv_amax_zero, dim3(1), dim3(1), 0, s, acc);
-      hipLaunchKernelGGL(nv_amax_kernel, dim3(grid_for(nchunks, 8)), dim3(kThreads), 0, s, xv,
+      int64_t ablocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+      if (ablocks > 1024) ablocks = 1024;     // ~4 per CU: 1024 atomics at most
+      if (ablocks < 1) ablocks = 1;
+      hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)ablocks), dim3(kThreads), 0, s, xv,
                          nchunks, acc);
       hipLaunchKernelGGL(nv_gs_finalize, dim3(1), dim3(1), 0, s, gs);
     }

@@ -65,19 +65,10 @@ __device__ __forceinline__ void emit(const Y8& y, int64_t row, int64_t chunk, in
   }
   m = quad_max_u32(m);
   uint32_t sb = mx_scale_byte<EMAX>(m);
-  float inv = mx_inv_scale(sb);
   if (MODE == kMXFP8) {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w0 |= e4m3_code(y.f[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w1 |= e4m3_code(y.f[4 + i] * inv) << (8 * i);
-    reinterpret_cast<uint2*>(q + row * h)[chunk] = make_uint2(w0, w1);
+    reinterpret_cast<uint2*>(q + row * h)[chunk] = mx_fp8x8(y.f, sb);
   } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_code(y.f[i] * inv) << (4 * i);
-    reinterpret_cast<uint32_t*>(q + row * (h / 2))[chunk] = w;
+    reinterpret_cast<uint32_t*>(q + row * (h / 2))[chunk] = mx_fp4x8(y.f, sb);
   }
   if ((chunk & 3) == 0) sf[row * (h / 32) + (chunk >> 2)] = (uint8_t)sb;
 }
