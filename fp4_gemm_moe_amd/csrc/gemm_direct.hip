@@ -17,7 +17,7 @@
 namespace hq {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves = 4-way K split
+constexpr int kThreads = 256;   // 4 waves = 4-way K split (NVFP4 and multi-fragment tiles)
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
@@ -72,11 +72,14 @@ __device__ __forceinline__ void load_slice(const uint8_t* row_codes, const uint8
   sc = kg < kgroups ? (int)row_sf[kg] : 127;
 }
 
-template <int FMT, int FM, int FN>
-__global__ __launch_bounds__(kThreads) void mx_gemm_direct(GemmArgs p) {
+// NW waves split K (wave w takes K steps w, w + NW, ...), U steps per trip
+// so that U loads per operand are in flight per wave; the NW partial tiles
+// are summed through LDS.
+template <int FMT, int FM, int FN, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void mx_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
-  __shared__ v4f red[3][FM * FN][64];
+  __shared__ v4f red[NW - 1][FM * FN][64];
 
   const int G = p.num_groups;
   const int NT = (int)((p.n + TN - 1) / TN);
@@ -123,19 +126,18 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_direct(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int t = w; t < ksteps; t += 8) {
-      // two K steps per trip (t and t + 4) so twice the loads are in flight
-      v8i af[2][FM], bf[2][FN];
-      int sa[2][FM], sb[2][FN];
+    for (int t = w; t < ksteps; t += NW * U) {
+      v8i af[U][FM], bf[U][FN];
+      int sa[U][FM], sb[U][FN];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) load_slice<FMT>(arow[fm], asf[fm], t + 4 * u, q, kgroups, af[u][fm], sa[u][fm]);
+        for (int fm = 0; fm < FM; ++fm) load_slice<FMT>(arow[fm], asf[fm], t + NW * u, q, kgroups, af[u][fm], sa[u][fm]);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) load_slice<FMT>(brow[fn], bsf[fn], t + 4 * u, q, kgroups, bf[u][fn], sb[u][fn]);
+        for (int fn = 0; fn < FN; ++fn) load_slice<FMT>(brow[fn], bsf[fn], t + NW * u, q, kgroups, bf[u][fn], sb[u][fn]);
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -157,8 +159,9 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_direct(GemmArgs p) {
         const int64_t m = tr.row0 + fm * 16 + r16;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          v4f v = acc[fm][fn] + red[0][fm * FN + fn][lane] + red[1][fm * FN + fn][lane] +
-                  red[2][fm * FN + fn][lane];
+          v4f v = acc[fm][fn];
+#pragma unroll
+          for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           const int64_t n = n0 + fn * 16 + 4 * q;
           if (m < tr.row_end && n < p.n)
             store_bf16x4(p.out + m * p.n + n, v, bias ? bias + n : nullptr);
@@ -170,20 +173,25 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_direct(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------- NVFP4
-// E2M1 nibble -> FP32 value (exact).
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  float mag = e == 0 ? (m ? 0.5f : 0.0f) : __uint_as_float(((e + 126u) << 23) | (m << 22));
-  return (c & 8u) ? -mag : mag;
-}
-
 // 8 nibbles times one UE4M3 scale -> 8 BF16 (exact: the product has at most
-// 6 significant bits and lies in [2^-10, 2688]).
+// 6 significant bits and lies in [2^-10, 2688]).  Nibbles decode to FP32 with
+// the hardware FP4 conversion (scale 1), two per instruction; the products
+// are packed to BF16 two per instruction.
 __device__ __forceinline__ v8bf decode8(uint32_t w, float sc) {
-  v8s r;
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2f f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
+  v8bf r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (short)(__float_as_uint(e2m1_value((w >> (4 * j)) & 15u) * sc) >> 16);
-  return __builtin_bit_cast(v8bf, r);
+  for (int b = 0; b < 4; ++b) {
+    const v2bf h = __builtin_convertvector((v2f{f[b][0] * sc, f[b][1] * sc}), v2bf);
+    r[2 * b] = h[0];
+    r[2 * b + 1] = h[1];
+  }
+  return r;
 }
 
 // Lane slice for NVFP4: 32 elements [32 kb, 32 kb + 32) of a row (16 bytes)
@@ -209,11 +217,11 @@ __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8
   return s;
 }
 
-template <int FM, int FN>
-__global__ __launch_bounds__(kThreads) void nv_gemm_direct(GemmArgs p) {
+template <int FM, int FN, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void nv_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
-  __shared__ v4f red[3][FM * FN][64];
+  __shared__ v4f red[NW - 1][FM * FN][64];
 
   const int G = p.num_groups;
   const int NT = (int)((p.n + TN - 1) / TN);
@@ -258,32 +266,40 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_direct(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int t = w; t < ksteps; t += 4) {
-      const int kb = t * 4 + q;
-      const bool kin = kb < kblocks;
-      NvSlice as[FM], bs[FN];
+    for (int t0 = w; t0 < ksteps; t0 += NW * U) {
+      NvSlice as[U][FM], bs[U][FN];
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) as[fm] = nv_load(arow[fm], asf[fm], kb, kin);
+      for (int u = 0; u < U; ++u) {
+        const int kb = (t0 + NW * u) * 4 + q;
+        const bool kin = kb < kblocks;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) bs[fn] = nv_load(brow[fn], bsf[fn], kb, kin);
+        for (int fm = 0; fm < FM; ++fm) as[u][fm] = nv_load(arow[fm], asf[fm], kb, kin);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v8bf ad[FM], bd[FN];
+        for (int fn = 0; fn < FN; ++fn) bs[u][fn] = nv_load(brow[fn], bsf[fn], kb, kin);
+      }
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          uint32_t wd = s == 0 ? as[fm].codes.x : s == 1 ? as[fm].codes.y : s == 2 ? as[fm].codes.z : as[fm].codes.w;
-          ad[fm] = decode8(wd, s < 2 ? as[fm].s0 : as[fm].s1);
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v8bf ad[FM], bd[FN];
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const uint4 c = as[u][fm].codes;
+            const uint32_t wd = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+            ad[fm] = decode8(wd, s < 2 ? as[u][fm].s0 : as[u][fm].s1);
+          }
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const uint4 c = bs[u][fn].codes;
+            const uint32_t wd = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+            bd[fn] = decode8(wd, s < 2 ? bs[u][fn].s0 : bs[u][fn].s1);
+          }
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bd[fn], ad[fm], acc[fm][fn], 0, 0, 0);
         }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          uint32_t wd = s == 0 ? bs[fn].codes.x : s == 1 ? bs[fn].codes.y : s == 2 ? bs[fn].codes.z : bs[fn].codes.w;
-          bd[fn] = decode8(wd, s < 2 ? bs[fn].s0 : bs[fn].s1);
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bd[fn], ad[fm], acc[fm][fn], 0, 0, 0);
       }
     }
 
@@ -301,8 +317,9 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_direct(GemmArgs p) {
         const int64_t m = tr.row0 + fm * 16 + r16;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          v4f v = acc[fm][fn] + red[0][fm * FN + fn][lane] + red[1][fm * FN + fn][lane] +
-                  red[2][fm * FN + fn][lane];
+          v4f v = acc[fm][fn];
+#pragma unroll
+          for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           v = v * alpha;
           const int64_t n = n0 + fn * 16 + 4 * q;
           if (m < tr.row_end && n < p.n) store_bf16x4(p.out + m * p.n + n, v, nullptr);
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void nv_gemm_direct(GemmArgs p) {
 
 template <class K>
 hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int TN,
-                         const DeviceInfo& dev) {
+                         const DeviceInfo& dev, int threads = kThreads) {
   const int64_t NT = (p.n + TN - 1) / TN;
   int64_t gm_upper;
   if (p.form == kContiguous) gm_upper = (p.m_rows + TM - 1) / TM + p.num_groups;
@@ -326,7 +343,7 @@ hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int
   int64_t grid = (int64_t)cus * 8;
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -337,18 +354,20 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
   const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
   const int fm = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
   if (p.mode == kNVFP4) {
-    if (fm == 1) return launch_direct(s, nv_gemm_direct<1, 2>, p, 16, 32, dev);
-    if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2>, p, 32, 32, dev);
-    return launch_direct(s, nv_gemm_direct<4, 2>, p, 64, 32, dev);
+    if (fm == 1) return launch_direct(s, nv_gemm_direct<1, 2, 8, 2>, p, 16, 32, dev, 512);
+    if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
+    return launch_direct(s, nv_gemm_direct<4, 2, 4, 1>, p, 64, 32, dev);
   }
+  // one 16-row fragment (skinny M): weights stream once, so 8 waves x 4
+  // steps of loads in flight per workgroup
   if (p.mode == kMXFP8) {
-    if (fm == 1) return launch_direct(s, mx_gemm_direct<0, 1, 1>, p, 16, 16, dev);
-    if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2>, p, 32, 32, dev);
-    return launch_direct(s, mx_gemm_direct<0, 4, 4>, p, 64, 64, dev);
+    if (fm == 1) return launch_direct(s, mx_gemm_direct<0, 1, 1, 8, 4>, p, 16, 16, dev, 512);
+    if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2, 4, 2>, p, 32, 32, dev);
+    return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2>, p, 64, 64, dev);
   }
-  if (fm == 1) return launch_direct(s, mx_gemm_direct<4, 1, 1>, p, 16, 16, dev);
-  if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2>, p, 32, 32, dev);
-  return launch_direct(s, mx_gemm_direct<4, 4, 4>, p, 64, 64, dev);
+  if (fm == 1) return launch_direct(s, mx_gemm_direct<4, 1, 1, 8, 4>, p, 16, 16, dev, 512);
+  if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2, 4, 2>, p, 32, 32, dev);
+  return launch_direct(s, mx_gemm_direct<4, 4, 4, 4, 2>, p, 64, 64, dev);
 }
 
 }  // namespace hq
