@@ -106,6 +106,10 @@ constexpr int WT = 128;                     // wave tile (square)
 constexpr int SROW = 128;                   // bytes of a row per stage
 constexpr int LOADS = BM * (SROW / 16) / THREADS;   // 16-byte loads per operand per thread (8)
 constexpr int kStores = 32;                 // output stores per thread per tile
+// MFMA row ahead of which a step issues the next step's loads: as early as
+// possible for FP8; one row in for FP4 (measured faster).
+template <int FMT>
+constexpr int kDmaRow = FMT == 0 ? 0 : 1;
 
 template <int FMT>
 struct Cfg {
@@ -324,7 +328,18 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     return (int)((d[plane] >> (8 * byte)) & 0xFFu);
   };
 
-  auto step = [&](const uint8_t* cur) {
+  // `mid()` runs once, ahead of the matrix instructions of MFMA row
+  // kDmaRow (row index 4 v + i) -- where the next step's loads are issued.
+  // pin(): keeps a step's matrix instructions ahead of the barrier that
+  // follows it where branches come next (the compiler would otherwise sink
+  // them past it).
+  auto pin = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  };
+  auto step = [&](const uint8_t* cur, auto&& mid) {
     const uint8_t* la = cur + wm * WT * SROW;
     const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
     const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
@@ -350,6 +365,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
         if (i < 3) fan = rd(la, i + 1, v);
         else if (v + 1 < SUB) fan = rd(la, 0, v + 1);
         if (v + 1 < SUB) fbn[i] = rd(lb, i, v + 1);
+        if (4 * v + i == kDmaRow<FMT>) mid();
         __builtin_amdgcn_sched_barrier(0);
         const v8i af = op(fa);
 #pragma unroll
@@ -389,12 +405,23 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     // Steps 0 .. nk-2.  Step 1's loads were issued with step 0's, before the
     // previous tile's stores; step k >= 1 issues step k + 1 into the stage
     // step k - 1 used.
-    for (int k = 0; k + 1 < nk; ++k) {
-      if (k >= 1) issue<FMT>(tl, lo, k + 1, smem + (st ^ 1) * C::STAGE, w);
-      step(smem + st * C::STAGE);
+    auto nothing = []() {};
+    if (nk > 1) {
+      // step 0: step 1's loads were issued with step 0's, before the previous
+      // tile's stores, which stay in flight
+      step(smem + st * C::STAGE, nothing);
+      pin();
       __builtin_amdgcn_sched_barrier(0);
-      if (k == 0 && prior_stores) wait_vm<kStores>();   // stores stay in flight
+      if (prior_stores) wait_vm<kStores>();
       else wait_vm<0>();
+      bar();
+      st ^= 1;
+    }
+    for (int k = 1; k + 1 < nk; ++k) {
+      const uint8_t* nxt = smem + (st ^ 1) * C::STAGE;
+      step(smem + st * C::STAGE, [&]() { issue<FMT>(tl, lo, k + 1, nxt, w); });
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<0>();
       bar();
       st ^= 1;
     }
@@ -406,7 +433,8 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
       tn = make_tile(p, tt, total_gm, NT, mt_per, t_next);
       issue<FMT>(tn, lo, 0, smem + (st ^ 1) * C::STAGE, w);
     }
-    step(smem + st * C::STAGE);
+    step(smem + st * C::STAGE, []() {});
+    pin();
     bar();                            // stage `st` is free
     if (has_next && nk > 1) issue<FMT>(tn, lo, 1, smem + st * C::STAGE, w);
 
