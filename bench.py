@@ -334,7 +334,7 @@ def run_sweep(args, torch, hq, synth):
                       "GB/s": round(bytes_ / (t * 1e-6) / 1e9, 1),
                       "bound": "hbm" if bytes_ / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12) else "mfma",
                       "t_ideal_us": round(t_ideal, 2), "roofline_frac": round(t_ideal / t, 3),
-                      "kernel": "direct" if m <= 16 else ("tiled" if mode != "nvfp4" else "direct_bf16")})
+                      "kernel": "direct" if m <= 16 else "tiled"})
                 del x, aq, asf, out
             del ring, wq, wsf
         del w

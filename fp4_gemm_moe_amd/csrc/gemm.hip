@@ -1,9 +1,8 @@
 // GEMM dispatch by mode, form and shape (the M-tiered dispatch of the
 // flashrt/fp4-gemm page, re-chosen for gfx950):
-//   * MX modes with K a multiple of the 128-byte K step and more than 16 rows
-//     per group: the LDS-tiled persistent kernel;
-//   * skinny M (<= 16 rows per group), any other K, and NVFP4: the direct
-//     kernel.
+//   * more than 16 rows per group and K a multiple of the K step (128 for
+//     MXFP8, 256 for MXFP4 and NVFP4): the LDS-tiled persistent kernel;
+//   * skinny M (<= 16 rows per group) and any other K: the direct kernel.
 #include "gemm_common.hpp"
 
 namespace hq {

@@ -8,10 +8,11 @@
 //     re-read from cache, and the K split keeps enough waves busy;
 //   * any K with k % 32 == 0 (a lane's K slice is exactly one 32-group, so a
 //     ragged K tail is a per-lane predicate: zero codes, unit scale);
-//   * NVFP4 (UE4M3 scales per 16 cannot be folded into the E8M0-scaled
-//     instruction, so codes are decoded to BF16 -- exactly: an E2M1 value
-//     times a UE4M3 value has at most 6 significant bits -- and multiplied on
-//     the BF16 matrix cores; alpha = g_A * g_B is applied in FP32).
+//   * NVFP4 in those shapes (UE4M3 scales per 16 cannot be folded into the
+//     E8M0-scaled instruction, so codes are decoded to BF16 -- exactly: an
+//     E2M1 value times a UE4M3 value has at most 6 significant bits -- and
+//     multiplied on the BF16 matrix cores; alpha = g_A * g_B is applied in
+//     FP32).
 #include "gemm_common.hpp"
 
 namespace hq {
@@ -19,7 +20,6 @@ namespace {
 
 constexpr int kThreads = 256;   // 4 waves = 4-way K split (NVFP4 and multi-fragment tiles)
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 
 // Resolves linear group-m-tile gm to (group, first row, row end).
@@ -173,27 +173,6 @@ __global__ __launch_bounds__(NW * 64) void mx_gemm_direct(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------- NVFP4
-// 8 nibbles times one UE4M3 scale -> 8 BF16 (exact: the product has at most
-// 6 significant bits and lies in [2^-10, 2688]).  Nibbles decode to FP32 with
-// the hardware FP4 conversion (scale 1), two per instruction; the products
-// are packed to BF16 two per instruction.
-__device__ __forceinline__ v8bf decode8(uint32_t w, float sc) {
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  const v2f f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
-  v8bf r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const v2bf h = __builtin_convertvector((v2f{f[b][0] * sc, f[b][1] * sc}), v2bf);
-    r[2 * b] = h[0];
-    r[2 * b + 1] = h[1];
-  }
-  return r;
-}
-
 // Lane slice for NVFP4: 32 elements [32 kb, 32 kb + 32) of a row (16 bytes)
 // and the two UE4M3 scales of its 16-groups.  The four BF16 MFMAs of one K
 // step consume its elements 8s..8s+7 (s = 0..3); the same K permutation is

@@ -1,5 +1,5 @@
-// LDS-tiled, double-buffered scaled-MFMA GEMM for the MX modes (MXFP8 and
-// MXFP4) -- the large-M tier of the flashrt/fp4-gemm page's M-tiered dispatch
+// LDS-tiled, double-buffered GEMM for the MX modes (MXFP8 and MXFP4, scaled
+// MFMA) and NVFP4 (exact BF16 decode, BF16 MFMA) -- the large-M tier of the flashrt/fp4-gemm page's M-tiered dispatch
 // and the grouped MoE GEMMs of the HALOps "GEMM" page (group_contiguous_gemm,
 // group_masked_gemm, batch_gemm sections).
 //
@@ -110,10 +110,13 @@ constexpr int kStores = 32;                 // output stores per thread per tile
 // possible for FP8; one row in for FP4 (measured faster).
 template <int FMT>
 constexpr int kDmaRow = FMT == 0 ? 0 : 1;
+constexpr int kNV = 2;                      // format tag of the NVFP4 instantiation
 
 template <int FMT>
 struct Cfg {
-  static constexpr int SB = FMT == 0 ? 4 : 8;       // scale bytes per row per stage
+  // scale bytes per row per stage: 128 FP8 / 256 FP4 elements per stage in
+  // E8M0 groups of 32, or 256 NVFP4 elements in UE4M3 groups of 16
+  static constexpr int SB = FMT == 0 ? 4 : (FMT == 4 ? 8 : 16);
   static constexpr int PLANES = SB / 4;
   static constexpr int A_BYTES = BM * SROW;
   static constexpr int B_BYTES = BN * SROW;
@@ -340,6 +343,73 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
       for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
   auto step = [&](const uint8_t* cur, auto&& mid) {
+    if constexpr (FMT == kNV) {
+      // NVFP4: codes decode exactly to BF16 (E2M1 value x UE4M3 scale, at
+      // most 6 significant bits) and multiply on the BF16 matrix cores,
+      // V_MFMA_F32_32X32X16_BF16.  A stage is 4 phases of 64 K; in phase q a
+      // lane reads 16-byte chunk 2q + h of each fragment row (32 codes) and
+      // scale dword q of the row (the 4 UE4M3 bytes of the phase's 16-groups;
+      // this lane group's are bytes 2h and 2h + 1).  Sub-step u of the phase
+      // multiplies codes 8u .. 8u + 7 of the lane's chunk (16-group 2h + u/2);
+      // both operands use this same K order, so the products pair up.
+      const uint8_t* la = cur + wm * WT * SROW;
+      const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
+      const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
+      const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WT + r32) * 4;
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      uint4 ca[4], cb[4], can[4], cbn[4];
+      uint32_t sa[4], sb[4], san[4], sbn[4];
+      auto load_phase = [&](int q, uint4 (&xa)[4], uint4 (&xb)[4], uint32_t (&ya)[4], uint32_t (&yb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xa[i] = rd16(la, i, 2 * q);
+          xb[i] = rd16(lb, i, 2 * q);
+          ya[i] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
+          yb[i] = lds_read4(lsb + q * BN * 4 + 32 * i * 4);
+        }
+      };
+      auto word = [](const uint4& c, int u) -> uint32_t {
+        return u == 0 ? c.x : (u == 1 ? c.y : (u == 2 ? c.z : c.w));
+      };
+      load_phase(0, ca, cb, sa, sb);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q + 1 < 4) load_phase(q + 1, can, cbn, san, sbn);
+        if (q == 0) mid();
+        __builtin_amdgcn_sched_barrier(0);
+        v2f fa[4], fb[4];        // this lane group's two UE4M3 scales per row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa[i] >> (16 * h), 1.0f, false);
+          fb[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[i] >> (16 * h), 1.0f, false);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v8bf da[4], db[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            da[i] = decode8(word(ca[i], u), fa[i][u >> 1]);
+            db[i] = decode8(word(cb[i], u), fb[i][u >> 1]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j], da[i], acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + 1 < 4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ca[i] = can[i];
+            cb[i] = cbn[i];
+            sa[i] = san[i];
+            sb[i] = sbn[i];
+          }
+        }
+      }
+      return;
+    }
     const uint8_t* la = cur + wm * WT * SROW;
     const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
     const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
@@ -449,6 +519,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
     const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
+    const float alpha = FMT == kNV ? p.alpha[tl.g] : 1.0f;   // NVFP4: g_A * g_B per group
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v4f bq[4];
@@ -467,8 +538,12 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
         uint32_t pk[4][2];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          pk[b][0] = pack_bf16x2(acc[i][j][4 * b] + bq[b][0], acc[i][j][4 * b + 1] + bq[b][1]);
-          pk[b][1] = pack_bf16x2(acc[i][j][4 * b + 2] + bq[b][2], acc[i][j][4 * b + 3] + bq[b][3]);
+          float f[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            f[r] = FMT == kNV ? acc[i][j][4 * b + r] * alpha : acc[i][j][4 * b + r] + bq[b][r];
+          pk[b][0] = pack_bf16x2(f[0], f[1]);
+          pk[b][1] = pack_bf16x2(f[2], f[3]);
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
@@ -529,7 +604,6 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
 }  // namespace
 
 bool tiled_supported(const GemmArgs& p) {
-  if (p.mode == kNVFP4) return false;
   const int64_t step = p.mode == kMXFP8 ? 128 : 256;
   if (p.k % step != 0) return false;
   if ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 3) return false;
@@ -540,6 +614,7 @@ bool tiled_supported(const GemmArgs& p) {
 
 hipError_t launch_gemm_tiled(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
   if (p.mode == kMXFP8) return launch_tiled_cfg<0>(s, p, dev);
+  if (p.mode == kNVFP4) return launch_tiled_cfg<kNV>(s, p, dev);
   return launch_tiled_cfg<4>(s, p, dev);
 }
 
