@@ -100,12 +100,7 @@ __device__ __forceinline__ v16f mfma32(v8i w, v8i x, v16f acc, int sw, int sx) {
 }
 
 constexpr int BM = 256, BN = 256;
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * 64;
-constexpr int WT = 128;                     // wave tile (square)
 constexpr int SROW = 128;                   // bytes of a row per stage
-constexpr int LOADS = BM * (SROW / 16) / THREADS;   // 16-byte loads per operand per thread (8)
-constexpr int kStores = 32;                 // output stores per thread per tile
 // MFMA row ahead of which a step issues the next step's loads: as early as
 // possible for FP8; one row in for FP4 (measured faster).
 template <int FMT>
@@ -114,6 +109,15 @@ constexpr int kNV = 2;                      // format tag of the NVFP4 instantia
 
 template <int FMT>
 struct Cfg {
+  // 32x32 fragments per wave along M and N: FP8 and NVFP4 run 4 waves of
+  // 128 x 128, FP4 8 waves (two per SIMD) of 128 x 64 (measured faster)
+  static constexpr int FI = 4, FJ = FMT == 4 ? 2 : 4;
+  static constexpr int WTM = 32 * FI, WTN = 32 * FJ;    // wave tile
+  static constexpr int WGN = BN / WTN;                  // waves along N
+  static constexpr int WAVES = (BM / WTM) * WGN;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int LOADS = BM * (SROW / 16) / THREADS;   // 16-byte loads per operand per thread
+  static constexpr int kStores = FI * FJ * 2;           // output stores per thread per tile
   // scale bytes per row per stage: 128 FP8 / 256 FP4 elements per stage in
   // E8M0 groups of 32, or 256 NVFP4 elements in UE4M3 groups of 16
   static constexpr int SB = FMT == 0 ? 4 : (FMT == 4 ? 8 : 16);
@@ -121,7 +125,10 @@ struct Cfg {
   static constexpr int A_BYTES = BM * SROW;
   static constexpr int B_BYTES = BN * SROW;
   static constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * SB;
-  static constexpr int OPS = 2 * LOADS + 2 * PLANES;  // vector-memory ops per stage per thread
+  // vector-memory ops per stage per thread: each wave loads the scale
+  // dwords of 512 / WAVES rows (of A or B with 8 waves, of both with 4)
+  static constexpr int SOPS = (BM + BN) / (WAVES * 64);
+  static constexpr int OPS = 2 * LOADS + SOPS * PLANES;
 };
 
 // Where a tile sits (uniform): group, first row, row end, first column, and
@@ -180,28 +187,32 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TileTable& tt
 // fills LDS rows [(i*4 + w) * 8, +8) of the A and of the B tile; lane j ->
 // row + j/8, physical chunk j % 8, logical chunk (j % 8) ^ swz(row).  Scale
 // dwords: wave w loads rows [64w, 64w + 64).
+template <int FMT>
 struct LoadOffsets {
-  uint32_t tile[LOADS];
+  uint32_t tile[Cfg<FMT>::LOADS];
   uint32_t scale;
 };
 
-__device__ __forceinline__ LoadOffsets make_offsets(const GemmArgs& p, int w, int lane) {
-  LoadOffsets o;
+template <int FMT>
+__device__ __forceinline__ LoadOffsets<FMT> make_offsets(const GemmArgs& p, int w, int lane) {
+  constexpr int LOADS = Cfg<FMT>::LOADS, WAVES = Cfg<FMT>::WAVES;
+  LoadOffsets<FMT> o;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int row = (i * WAVES + w) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
     o.tile[i] = (uint32_t)(row * p.lda + c * 16);
   }
-  o.scale = (uint32_t)((w * 64 + lane) * p.ldsf);
+  o.scale = (uint32_t)((((w * 64) % BM) + lane) * p.ldsf);
   return o;
 }
 
 // Issues K step k of tile `tl` into LDS stage `st`: Cfg<FMT>::OPS operations.
 template <int FMT>
-__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets& o, int k, const uint8_t* st,
+__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o, int k, const uint8_t* st,
                                       int w) {
   using C = Cfg<FMT>;
+  constexpr int LOADS = C::LOADS, WAVES = C::WAVES;
   const uint32_t base = ufirst(lds_addr(st));
   const uint32_t la = base + w * 1024;
   const uint32_t lb = la + C::A_BYTES;
@@ -212,15 +223,25 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets& o, int 
   for (int i = 0; i < LOADS; ++i) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) dma16(rb, o.tile[i], lb + i * WAVES * 1024);
-  // scale planes: dword plane h of row r at plane h * rows + r
-  const uint32_t lsa = base + C::A_BYTES + C::B_BYTES + w * 256;
+  // scale planes: dword plane h of row r at plane h * rows + r.  With four
+  // waves wave w loads rows [64 w, 64 w + 64) of A and of B; with eight,
+  // waves 0-3 those rows of A and waves 4-7 of B.
+  const uint32_t lsa = base + C::A_BYTES + C::B_BYTES + ((w * 64) % BM) * 4;
   const uint32_t lsb = lsa + BM * C::SB;
   const __amdgpu_buffer_rsrc_t rsa = rsrc(tl.sa + ks, tl.sa_bytes - ks);
   const __amdgpu_buffer_rsrc_t rsb = rsrc(tl.sb + ks, tl.sb_bytes - ks);
+  if constexpr (C::SOPS == 2) {
 #pragma unroll
-  for (int h = 0; h < C::PLANES; ++h) {
-    dma4(rsa, o.scale + 4 * h, lsa + h * BM * 4);
-    dma4(rsb, o.scale + 4 * h, lsb + h * BN * 4);
+    for (int h = 0; h < C::PLANES; ++h) {
+      dma4(rsa, o.scale + 4 * h, lsa + h * BM * 4);
+      dma4(rsb, o.scale + 4 * h, lsb + h * BN * 4);
+    }
+  } else {
+    const bool is_a = w * 64 < BM;
+    const __amdgpu_buffer_rsrc_t rs = is_a ? rsa : rsb;
+    const uint32_t ls = is_a ? lsa : lsb;
+#pragma unroll
+    for (int h = 0; h < C::PLANES; ++h) dma4(rs, o.scale + 4 * h, ls + h * BM * 4);
   }
 }
 
@@ -248,8 +269,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
+__global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
+  constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
+  constexpr int kStores = C::kStores;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TileTable tt;
 
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   const int tid = threadIdx.x;
   const int w = ufirst(tid >> 6);                           // wave index (uniform)
   const int lane = tid & 63;
-  const int wm = w >> 1, wn = w & 1;                        // 2 x 2 wave grid
+  const int wm = w / WGN, wn = w % WGN;                     // wave grid (M x N)
   const int h = lane >> 5, r32 = lane & 31;
   const int nk = (int)(p.lda / SROW);
 
@@ -278,7 +301,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   int t = slot;
   if (t >= total) return;
 
-  const LoadOffsets lo = make_offsets(p, w, lane);
+  const LoadOffsets<FMT> lo = make_offsets<FMT>(p, w, lane);
 
   // Fragment-read offsets.  Fragment row i of the wave tile is LDS row
   // 128 wm + 32 i + r32 (A) / 128 wn + 32 i + r32 (B); its swizzle is
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     return lds_read16(wbase + i * 32 * SROW + xo[(c ^ (4 * (i & 1))) >> 1]);
   };
 
-  v16f acc[4][4];
+  v16f acc[FI][FJ];
 
   // One K step on stage `cur`.  A step is SUB matrix-core sub-steps (two of
   // K 64 for FP8, four of K 64 for FP4); sub-step v reads, per fragment row,
@@ -338,9 +361,9 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   // them past it).
   auto pin = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < FJ; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
   auto step = [&](const uint8_t* cur, auto&& mid) {
     if constexpr (FMT == kNV) {
@@ -352,20 +375,23 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
       // this lane group's are bytes 2h and 2h + 1).  Sub-step u of the phase
       // multiplies codes 8u .. 8u + 7 of the lane's chunk (16-group 2h + u/2);
       // both operands use this same K order, so the products pair up.
-      const uint8_t* la = cur + wm * WT * SROW;
-      const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
-      const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
-      const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WT + r32) * 4;
+      const uint8_t* la = cur + wm * WTM * SROW;
+      const uint8_t* lb = cur + C::A_BYTES + wn * WTN * SROW;
+      const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WTM + r32) * 4;
+      const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WTN + r32) * 4;
       typedef float v2f __attribute__((ext_vector_type(2)));
-      uint4 ca[4], cb[4], can[4], cbn[4];
-      uint32_t sa[4], sb[4], san[4], sbn[4];
-      auto load_phase = [&](int q, uint4 (&xa)[4], uint4 (&xb)[4], uint32_t (&ya)[4], uint32_t (&yb)[4]) {
+      uint4 ca[FI], cb[FJ], can[FI], cbn[FJ];
+      uint32_t sa[FI], sb[FJ], san[FI], sbn[FJ];
+      auto load_phase = [&](int q, uint4 (&xa)[FI], uint4 (&xb)[FJ], uint32_t (&ya)[FI], uint32_t (&yb)[FJ]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < FI; ++i) {
           xa[i] = rd16(la, i, 2 * q);
-          xb[i] = rd16(lb, i, 2 * q);
           ya[i] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
-          yb[i] = lds_read4(lsb + q * BN * 4 + 32 * i * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          xb[j] = rd16(lb, j, 2 * q);
+          yb[j] = lds_read4(lsb + q * BN * 4 + 32 * j * 4);
         }
       };
       auto word = [](const uint4& c, int u) -> uint32_t {
@@ -377,76 +403,77 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
         if (q + 1 < 4) load_phase(q + 1, can, cbn, san, sbn);
         if (q == 0) mid();
         __builtin_amdgcn_sched_barrier(0);
-        v2f fa[4], fb[4];        // this lane group's two UE4M3 scales per row
+        v2f fa[FI], fb[FJ];      // this lane group's two UE4M3 scales per row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa[i] >> (16 * h), 1.0f, false);
-          fb[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[i] >> (16 * h), 1.0f, false);
-        }
+        for (int i = 0; i < FI; ++i) fa[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa[i] >> (16 * h), 1.0f, false);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) fb[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[j] >> (16 * h), 1.0f, false);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          v8bf da[4], db[4];
+          v8bf da[FI], db[FJ];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            da[i] = decode8(word(ca[i], u), fa[i][u >> 1]);
-            db[i] = decode8(word(cb[i], u), fb[i][u >> 1]);
-          }
+          for (int i = 0; i < FI; ++i) da[i] = decode8(word(ca[i], u), fa[i][u >> 1]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int j = 0; j < FJ; ++j) db[j] = decode8(word(cb[j], u), fb[j][u >> 1]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j], da[i], acc[i][j], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (q + 1 < 4) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < FI; ++i) {
             ca[i] = can[i];
-            cb[i] = cbn[i];
             sa[i] = san[i];
-            sb[i] = sbn[i];
+          }
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) {
+            cb[j] = cbn[j];
+            sb[j] = sbn[j];
           }
         }
       }
       return;
     }
-    const uint8_t* la = cur + wm * WT * SROW;
-    const uint8_t* lb = cur + C::A_BYTES + wn * WT * SROW;
-    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WT + r32) * 4;
-    const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WT + r32) * 4;
+    const uint8_t* la = cur + wm * WTM * SROW;
+    const uint8_t* lb = cur + C::A_BYTES + wn * WTN * SROW;
+    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WTM + r32) * 4;
+    const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WTN + r32) * 4;
     Frag fa = rd(la, 0, 0);
-    Frag fb[4], fbn[4];
+    Frag fb[FJ], fbn[FJ];
     fb[0] = rd(lb, 0, 0);
-    uint32_t asc[4][C::PLANES], bsc[4][C::PLANES];
+    uint32_t asc[FI][C::PLANES], bsc[FJ][C::PLANES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < C::PLANES; ++q) {
 #pragma unroll
-      for (int q = 0; q < C::PLANES; ++q) {
-        bsc[i][q] = lds_read4(lsb + q * BN * 4 + 32 * i * 4);
-        asc[i][q] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
-      }
+      for (int j = 0; j < FJ; ++j) bsc[j][q] = lds_read4(lsb + q * BN * 4 + 32 * j * 4);
 #pragma unroll
-    for (int j = 1; j < 4; ++j) fb[j] = rd(lb, j, 0);
+      for (int i = 0; i < FI; ++i) asc[i][q] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
+    }
+#pragma unroll
+    for (int j = 1; j < FJ; ++j) fb[j] = rd(lb, j, 0);
 #pragma unroll
     for (int v = 0; v < SUB; ++v) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < FI; ++i) {
         Frag fan = fa;
-        if (i < 3) fan = rd(la, i + 1, v);
+        if (i + 1 < FI) fan = rd(la, i + 1, v);
         else if (v + 1 < SUB) fan = rd(la, 0, v + 1);
-        if (v + 1 < SUB) fbn[i] = rd(lb, i, v + 1);
+        if (v + 1 < SUB && i < FJ) fbn[i] = rd(lb, i, v + 1);
         if (4 * v + i == kDmaRow<FMT>) mid();
         __builtin_amdgcn_sched_barrier(0);
         const v8i af = op(fa);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FJ; ++j)
           acc[i][j] = mfma32<FMT>(op(fb[j]), af, acc[i][j], sc(bsc[j], v), sc(asc[i], v));
         __builtin_amdgcn_sched_barrier(0);
         fa = fan;
       }
       if (v + 1 < SUB) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = fbn[j];
+        for (int j = 0; j < FJ; ++j) fb[j] = fbn[j];
       }
     }
   };
@@ -466,9 +493,9 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   bool prior_stores = false;
   while (true) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -521,11 +548,11 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
     const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
     const float alpha = FMT == kNV ? p.alpha[tl.g] : 1.0f;   // NVFP4: g_A * g_B per group
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FJ; ++j) {
       v4f bq[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int64_t n = tl.n0 + wn * WT + j * 32 + 8 * b + 4 * h;
+        const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * b + 4 * h;
         bq[b] = v4f{0.f, 0.f, 0.f, 0.f};
         if (bias != nullptr && n < p.n) {
           uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
@@ -533,8 +560,8 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t mr = wm * WT + i * 32 + r32;             // row within the tile
+      for (int i = 0; i < FI; ++i) {
+        const int64_t mr = wm * WTM + i * 32 + r32;            // row within the tile
         uint32_t pk[4][2];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -556,7 +583,7 @@ __global__ __launch_bounds__(THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
           uint32_t r1 = (uint32_t)__shfl_xor((int)s1w, 32, 64);
           typedef uint32_t v4u __attribute__((ext_vector_type(4)));
           v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
-          const int64_t n = tl.n0 + wn * WT + j * 32 + 8 * (h == 0 ? bl : bh);
+          const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * (h == 0 ? bl : bh);
           const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
           __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
         }
@@ -597,7 +624,7 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (tiles < grid) grid = tiles;
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((mx_gemm_tiled<FMT>), dim3((unsigned)grid), dim3(THREADS), smem, s, p);
+  hipLaunchKernelGGL((mx_gemm_tiled<FMT>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, p);
   return hipGetLastError();
 }
 
