@@ -80,10 +80,11 @@ struct TileTable {
 
 // Fills the table (all threads must call) and returns the total number of
 // group m-tiles.  Rows are clamped as documented for device-side values.
+template <int NT>
 __device__ inline int build_tile_table(const GemmArgs& p, int TM, TileTable& t) {
   const int G = p.num_groups;
   if (p.form == kContiguous) {
-    load_clamped_ends(t.mt_prefix, p.group_end, G, p.m_rows);   // reuse as scratch
+    load_clamped_ends<NT>(t.mt_prefix, p.group_end, G, p.m_rows);   // reuse as scratch
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
       int e = t.mt_prefix[g];
       int s = g > 0 ? t.mt_prefix[g - 1] : 0;
@@ -104,7 +105,7 @@ __device__ inline int build_tile_table(const GemmArgs& p, int TM, TileTable& t) 
   __syncthreads();
   for (int g = threadIdx.x; g < G; g += blockDim.x) t.mt_prefix[g] = (t.count[g] + TM - 1) / TM;
   __syncthreads();
-  return block_scan_1024(t.mt_prefix, G, OpAdd(), 0);
+  return block_scan_1024<NT>(t.mt_prefix, G, OpAdd(), 0);
 }
 
 // Group owning linear group-m-tile index gm (prefix is inclusive).

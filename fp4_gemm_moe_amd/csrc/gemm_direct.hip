@@ -86,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void mx_gemm_direct(GemmArgs p) {
   const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
   int total_gm;
   if (p.form == kUniform) total_gm = G * mt_per;
-  else total_gm = build_tile_table(p, TM, tt);
+  else total_gm = build_tile_table<NW * 64>(p, TM, tt);
   const int total = total_gm * NT;
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void nv_gemm_direct(GemmArgs p) {
   const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
   int total_gm;
   if (p.form == kUniform) total_gm = G * mt_per;
-  else total_gm = build_tile_table(p, TM, tt);
+  else total_gm = build_tile_table<NW * 64>(p, TM, tt);
   const int total = total_gm * NT;
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;

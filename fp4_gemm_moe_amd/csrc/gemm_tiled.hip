@@ -131,6 +131,65 @@ struct Cfg {
   static constexpr int OPS = 2 * LOADS + SOPS * PLANES;
 };
 
+// Grouped forms: per group its end row and the inclusive prefixes of its
+// heavy and light m-tiles.  Where two waves share each SIMD (Cfg::WAVES > 4),
+// a group's last m-tile with at most WTM valid rows is light: only the waves
+// of its first WTM rows multiply, at about half a heavy tile's cost.  Heavy
+// m-tiles are numbered first and the grid walks its rounds in alternating
+// directions, so each workgroup's share of heavy and light tiles evens out.
+// With one wave per SIMD every m-tile counts as heavy.
+struct TiledTable {
+  int end[kMaxGroups];
+  int heavy[kMaxGroups];
+  int light[kMaxGroups];
+};
+
+__device__ __forceinline__ int64_t group_start(const GemmArgs& p, const TiledTable& t, int g) {
+  if (p.form == kContiguous) return g > 0 ? t.end[g - 1] : 0;
+  return (int64_t)g * p.slot_rows;
+}
+
+// First group whose inclusive prefix exceeds x.
+__device__ __forceinline__ int prefix_group(const int* pre, int G, int x) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] > x) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Fills the table (all threads must call); returns the number of group
+// m-tiles and sets n_heavy.  Device-side ends and counts are clamped as for
+// every grouped form.
+template <int FMT>
+__device__ int build_tiled_table(const GemmArgs& p, TiledTable& t, int& n_heavy) {
+  constexpr bool kSplit = Cfg<FMT>::WAVES > 4;
+  constexpr int WTM = Cfg<FMT>::WTM;
+  const int G = p.num_groups;
+  if (p.form == kContiguous) {
+    load_clamped_ends<Cfg<FMT>::THREADS>(t.end, p.group_end, G, p.m_rows);
+  } else {
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+      const int64_t v = p.counts[g];
+      const int64_t c = v < 0 ? 0 : (v > p.slot_rows ? p.slot_rows : v);
+      t.end[g] = (int)((int64_t)g * p.slot_rows + c);
+    }
+    __syncthreads();
+  }
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int rows = (int)(t.end[g] - group_start(p, t, g));
+    const int full = rows / BM, rem = rows - full * BM;
+    const bool lt = kSplit && rem > 0 && rem <= WTM;
+    t.heavy[g] = full + (rem > 0 && !lt ? 1 : 0);
+    t.light[g] = lt ? 1 : 0;
+  }
+  __syncthreads();
+  n_heavy = block_scan_1024<Cfg<FMT>::THREADS>(t.heavy, G, OpAdd(), 0);
+  return n_heavy + block_scan_1024<Cfg<FMT>::THREADS>(t.light, G, OpAdd(), 0);
+}
+
 // Where a tile sits (uniform): group, first row, row end, first column, and
 // the byte bases / extents of its operands.
 struct Tile {
@@ -140,8 +199,8 @@ struct Tile {
   int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
 };
 
-__device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TileTable& tt, int total_gm,
-                                          int NT, int mt_per, int t) {
+__device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& tt, int total_gm,
+                                          int n_heavy, int NT, int mt_per, int t) {
   // blocks of 4 m-tiles x all n-tiles, walked n-major inside the block so 32
   // consecutive tiles = 4 m x 8 n
   const int blk = t / (4 * NT);
@@ -159,10 +218,16 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TileTable& tt
     row0 = gs + (int64_t)mt * BM;
     row_end = row0 + BM < gs + p.slot_rows ? row0 + BM : gs + p.slot_rows;
   } else {
-    g = tile_group(tt, p.num_groups, gm);
-    const int mt = gm - (g > 0 ? tt.mt_prefix[g - 1] : 0);
-    row0 = (int64_t)tt.start[g] + (int64_t)mt * BM;
-    const int64_t ge = (int64_t)tt.start[g] + tt.count[g];
+    int mt;
+    if (gm < n_heavy) {
+      g = prefix_group(tt.heavy, p.num_groups, gm);
+      mt = gm - (g > 0 ? tt.heavy[g - 1] : 0);
+    } else {                          // a light tile: the group's last m-tile
+      g = prefix_group(tt.light, p.num_groups, gm - n_heavy);
+      mt = tt.heavy[g] - (g > 0 ? tt.heavy[g - 1] : 0);
+    }
+    row0 = group_start(p, tt, g) + (int64_t)mt * BM;
+    const int64_t ge = tt.end[g];
     row_end = row0 + BM < ge ? row0 + BM : ge;
   }
   Tile tl;
@@ -176,9 +241,11 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TileTable& tt
   tl.b = uniform_ptr(p.b + brow0 * p.lda);
   tl.sa = uniform_ptr(p.sfa + tl.row0 * p.ldsf);
   tl.sb = uniform_ptr(p.sfb + brow0 * p.ldsf);
-  tl.a_bytes = (p.m_rows - tl.row0) * p.lda;
+  // A rows past the tile's valid rows (the next group's, or a masked slot's
+  // padding) are not fetched: the bounded loads fill them with zeros
+  tl.a_bytes = (tl.row_end - tl.row0) * p.lda;
   tl.b_bytes = (brows - brow0) * p.lda;
-  tl.sa_bytes = (p.m_rows - tl.row0) * p.ldsf;
+  tl.sa_bytes = (tl.row_end - tl.row0) * p.ldsf;
   tl.sb_bytes = (brows - brow0) * p.ldsf;
   return tl;
 }
@@ -207,13 +274,13 @@ __device__ __forceinline__ LoadOffsets<FMT> make_offsets(const GemmArgs& p, int 
   return o;
 }
 
-// Issues K step k of tile `tl` into LDS stage `st`: Cfg<FMT>::OPS operations.
+// Issues K step k of tile `tl` into the LDS stage at byte address `base`:
+// Cfg<FMT>::OPS operations.
 template <int FMT>
-__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o, int k, const uint8_t* st,
+__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o, int k, uint32_t base,
                                       int w) {
   using C = Cfg<FMT>;
   constexpr int LOADS = C::LOADS, WAVES = C::WAVES;
-  const uint32_t base = ufirst(lds_addr(st));
   const uint32_t la = base + w * 1024;
   const uint32_t lb = la + C::A_BYTES;
   const int64_t ka = (int64_t)k * SROW, ks = (int64_t)k * C::SB;
@@ -274,14 +341,14 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
   constexpr int kStores = C::kStores;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ TileTable tt;
+  __shared__ TiledTable tt;
 
   const int G0 = p.num_groups;
   const int NT = (int)((p.n + BN - 1) / BN);
   const int mt_per = p.form == kUniform ? (int)((p.slot_rows + BM - 1) / BM) : 0;
-  int total_gm;
+  int total_gm, n_heavy = 0;
   if (p.form == kUniform) total_gm = G0 * mt_per;
-  else total_gm = build_tile_table(p, BM, tt);
+  else total_gm = build_tiled_table<FMT>(p, tt, n_heavy);
   const int total = total_gm * NT;
 
   const int tid = threadIdx.x;
@@ -292,13 +359,17 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   const int nk = (int)(p.lda / SROW);
 
   // XCD-aware order: workgroup b runs on XCD b % 8; inside a round of
-  // gridDim tiles XCD x owns a contiguous run of tiles.
+  // gridDim tiles XCD x owns a contiguous run of tiles.  Rounds alternate
+  // direction: in odd rounds the workgroup at slot s takes the round's tile
+  // stride - 1 - s (a workgroup's tile index still grows round by round).
   const int nxcd = gridDim.x >= 8 ? 8 : 1;
   const int per_xcd = gridDim.x / nxcd;
   const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
   const int stride = per_xcd * nxcd;
   if ((int)blockIdx.x >= stride) return;
-  int t = slot;
+  auto tile_of = [&](int round) { return round * stride + ((round & 1) ? stride - 1 - slot : slot); };
+  int round = 0;
+  int t = tile_of(0);
   if (t >= total) return;
 
   const LoadOffsets<FMT> lo = make_offsets<FMT>(p, w, lane);
@@ -365,7 +436,16 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
       for (int j = 0; j < FJ; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
+  // A wave whose rows of the tile all lie past its valid rows (a group's last,
+  // partial tile; a masked slot's padding) only issues its share of the loads:
+  // no fragment reads, no matrix instructions.  It meets every barrier and
+  // runs the epilogue, whose stores then fall outside the tile's bounds.
+  bool active = true;
   auto step = [&](const uint8_t* cur, auto&& mid) {
+    if (!active) {
+      mid();
+      return;
+    }
     if constexpr (FMT == kNV) {
       // NVFP4: codes decode exactly to BF16 (E2M1 value x UE4M3 scale, at
       // most 6 significant bits) and multiply on the BF16 matrix cores,
@@ -478,12 +558,13 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
   };
 
-  Tile tl = make_tile(p, tt, total_gm, NT, mt_per, t);
+  Tile tl = make_tile(p, tt, total_gm, n_heavy, NT, mt_per, t);
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
-  issue<FMT>(tl, lo, 0, smem, w);
+  const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
+  issue<FMT>(tl, lo, 0, smem_lds, w);
   if (nk > 1) {
-    issue<FMT>(tl, lo, 1, smem + C::STAGE, w);
+    issue<FMT>(tl, lo, 1, smem_lds + C::STAGE, w);
     wait_vm<C::OPS>();
   } else {
     wait_vm<0>();
@@ -492,6 +573,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 
   bool prior_stores = false;
   while (true) {
+    active = wm * WTM < tl.row_end - tl.row0;
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -515,7 +597,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       st ^= 1;
     }
     for (int k = 1; k + 1 < nk; ++k) {
-      const uint8_t* nxt = smem + (st ^ 1) * C::STAGE;
+      const uint32_t nxt = smem_lds + (st ^ 1) * C::STAGE;
       step(smem + st * C::STAGE, [&]() { issue<FMT>(tl, lo, k + 1, nxt, w); });
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<0>();
@@ -523,17 +605,17 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       st ^= 1;
     }
     // last step: the next tile's step 0 goes into the other stage
-    const int t_next = t + stride;
+    const int t_next = tile_of(round + 1);
     const bool has_next = t_next < total;
     Tile tn = tl;
     if (has_next) {
-      tn = make_tile(p, tt, total_gm, NT, mt_per, t_next);
-      issue<FMT>(tn, lo, 0, smem + (st ^ 1) * C::STAGE, w);
+      tn = make_tile(p, tt, total_gm, n_heavy, NT, mt_per, t_next);
+      issue<FMT>(tn, lo, 0, smem_lds + (st ^ 1) * C::STAGE, w);
     }
     step(smem + st * C::STAGE, []() {});
     pin();
     bar();                            // stage `st` is free
-    if (has_next && nk > 1) issue<FMT>(tn, lo, 1, smem + st * C::STAGE, w);
+    if (has_next && nk > 1) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
 
     // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
     // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
@@ -596,6 +678,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     else wait_vm<kStores>();
     bar();
     t = t_next;
+    ++round;
     tl = tn;
     st ^= 1;
     prior_stores = true;

@@ -23,24 +23,26 @@ struct OpMax {
   __device__ int operator()(int a, int b) const { return a > b ? a : b; }
 };
 
-// In-place inclusive scan of s[0, n) (n <= 1024) by a 256-thread block.
-// Each thread scans 4 consecutive entries, waves scan their thread totals
-// with lane shuffles, and 4 wave totals are combined through LDS.  Returns
-// the scan's last value to every thread.  Must be reached by all threads.
-template <class Op>
+// In-place inclusive scan of s[0, n) (n <= 1024) by a block of NT threads
+// (a multiple of 64, at most 1024).  Each thread scans 1024 / NT consecutive
+// entries, waves scan their thread totals with lane shuffles, and the wave
+// totals are combined through LDS.  `op` must be associative with `identity`
+// neutral.  Returns the scan's last value to every thread.  Must be reached
+// by all threads.
+template <int NT, class Op>
 __device__ int block_scan_1024(int* s, int n, Op op, int identity) {
-  __shared__ int wsum[4];
+  static_assert(NT % 64 == 0 && NT >= 64 && NT <= 1024, "block of whole waves, at most 1024 threads");
+  constexpr int PER = 1024 / NT, NW = NT / 64;
+  __shared__ int wsum[NW];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int v[4];
+  int v[PER];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int idx = t * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int idx = t * PER + i;
     v[i] = idx < n ? s[idx] : identity;
+    if (i > 0) v[i] = op(v[i - 1], v[i]);
   }
-  v[1] = op(v[0], v[1]);
-  v[2] = op(v[1], v[2]);
-  v[3] = op(v[2], v[3]);
-  int x = v[3];
+  int x = v[PER - 1];
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     int y = __shfl_up(x, off, 64);
@@ -48,30 +50,34 @@ __device__ int block_scan_1024(int* s, int n, Op op, int identity) {
   }
   if (lane == 63) wsum[w] = x;
   __syncthreads();
-  int prefix = identity;
-  for (int j = 0; j < w; ++j) prefix = op(prefix, wsum[j]);
+  int prefix = identity, total = identity;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    if (j < w) prefix = op(prefix, wsum[j]);
+    total = op(total, wsum[j]);
+  }
   int excl = __shfl_up(x, 1, 64);
   if (lane == 0) excl = identity;
   excl = op(prefix, excl);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int idx = t * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int idx = t * PER + i;
     if (idx < n) s[idx] = op(excl, v[i]);
   }
-  int total = op(op(wsum[0], wsum[1]), op(wsum[2], wsum[3]));
   __syncthreads();
   return total;
 }
 
 // Loads group ends into s[0, G) as clamped, non-decreasing ends:
 // e'_g = min(max(e_0 .. e_g, 0), rows).
+template <int NT>
 __device__ inline void load_clamped_ends(int* s, const int32_t* group_end, int G, int64_t rows) {
   for (int i = threadIdx.x; i < G; i += blockDim.x) {
     int e = group_end[i];
     s[i] = e > 0 ? e : 0;
   }
   __syncthreads();
-  block_scan_1024(s, G, OpMax(), 0);
+  block_scan_1024<NT>(s, G, OpMax(), 0);
   for (int i = threadIdx.x; i < G; i += blockDim.x) {
     int64_t e = s[i];
     s[i] = (int)(e < rows ? e : rows);

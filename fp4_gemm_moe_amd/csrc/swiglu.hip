@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_quant_kernel(
     uint8_t* __restrict__ q, uint8_t* __restrict__ sf, const float* __restrict__ gs,
     float* __restrict__ y_debug) {
   __shared__ int s_end[kMaxGroups];
-  if (group_end != nullptr) load_clamped_ends(s_end, group_end, G, rows);
+  if (group_end != nullptr) load_clamped_ends<kThreads>(s_end, group_end, G, rows);
 
   float g = 1.0f, d = 6.0f;
   if (MODE == kNVFP4) {

@@ -244,6 +244,68 @@ def test_group_masked_matches_contiguous_with_garbage_padding(mode):
                                 U.deq(mode, b[e], sfb[e]), None if al is None else al[e], f"expert {e}")
 
 
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("form", ["contiguous", "masked"])
+def test_many_groups(mode, form):
+    """1024 groups (the limit): the group table fills every entry, tiles
+    outnumber the CUs several times over, and groups end in full, more than
+    half-full and at most half-full m-tiles (row counts around 128 and 256)."""
+    dev = U.require_gpu()
+    E, K, N = 1024, 256, 64
+    rng = np.random.default_rng(77)
+    if form == "contiguous":
+        counts = rng.integers(0, 200, size=E).astype(np.int32)
+        counts[rng.choice(E, 100, replace=False)] = 0
+        counts[:8] = [128, 129, 256, 257, 300, 1, 127, 383]
+    else:
+        Mmax = 160
+        counts = rng.integers(0, Mmax + 1, size=E).astype(np.int32)
+        counts[rng.choice(E, 100, replace=False)] = 0
+        counts[:6] = [128, 129, 160, 1, 127, 0]
+    U.banner(f"{form} {mode} E={E} rows={int(counts.sum())}")
+    ends = np.cumsum(counts).astype(np.int32)
+    starts = ends - counts
+    xa = synth.normal_bf16(rng, (int(ends[-1]), K))
+    a_c, sfa_c, ga = _quant(xa, mode)
+    xb = synth.normal_bf16(rng, (E * N, K), 0.05)
+    bq, bs, gb = _quant(xb, mode)
+    b, sfb = bq.reshape(E, N, -1), bs.reshape(E, N, -1)
+    al = None if ga is None else np.full(E, np.float32(ga * gb), np.float32)
+    alpha = None if al is None else torch.from_numpy(al).to(dev)
+    if form == "contiguous":
+        out = torch.full((len(xa), N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        hq.hq_group_contiguous_gemm(mode, U.dev_u8(a_c, dev), U.dev_u8(sfa_c, dev), U.dev_u8(b, dev),
+                                    U.dev_u8(sfb, dev), U.dev_i32(ends, dev), out, alpha=alpha)
+        torch.cuda.synchronize()
+        got = U.host_bits(out)
+        rows = [(starts[e], ends[e]) for e in range(E)]
+    else:
+        a_m = synth.garbage_bytes(5, (E * Mmax, a_c.shape[1]))
+        sfa_m = synth.garbage_bytes(6, (E * Mmax, sfa_c.shape[1]))
+        for e in range(E):
+            a_m[e * Mmax:e * Mmax + counts[e]] = a_c[starts[e]:ends[e]]
+            sfa_m[e * Mmax:e * Mmax + counts[e]] = sfa_c[starts[e]:ends[e]]
+        out = torch.full((E * Mmax, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        hq.hq_group_masked_gemm(mode, U.dev_u8(a_m, dev), U.dev_u8(sfa_m, dev), U.dev_u8(b, dev),
+                                U.dev_u8(sfb, dev), U.dev_i32(counts, dev), out, Mmax, alpha=alpha)
+        torch.cuda.synchronize()
+        gm = U.host_bits(out)
+        pad = np.ones(E * Mmax, bool)
+        for e in range(E):
+            pad[e * Mmax:e * Mmax + counts[e]] = False
+        assert np.all(gm[pad] == SENTINEL), "a padded row was written"
+        got = np.zeros((len(xa), N), np.uint16)
+        for e in range(E):
+            got[starts[e]:ends[e]] = gm[e * Mmax:e * Mmax + counts[e]]
+        rows = [(starts[e], ends[e]) for e in range(E)]
+    for e, (lo, hi) in enumerate(rows):
+        if hi > lo:
+            want = G.dense_gemm(mode, a_c[lo:hi], sfa_c[lo:hi], b[e], sfb[e],
+                                alpha=None if al is None else al[e])
+            U.assert_gemm_close(got[lo:hi], want, U.deq(mode, a_c[lo:hi], sfa_c[lo:hi]), U.deq(mode, b[e], sfb[e]),
+                                None if al is None else al[e], f"{form} group {e} ({hi - lo} rows)")
+
+
 def test_device_counts_are_clamped():
     """Out-of-range device values: a masked count above max_m covers the slot
     exactly; a negative count covers nothing; decreasing ends give empty
