@@ -264,7 +264,7 @@ def run_masked_fp4(args, torch, hq, synth):
     gbs = bytes_ / (ms * 1e-3) / 1e9
     cfg = {"workload": "moe_grouped_masked_mxfp4_E64_Mmax256_K7168_N4096", "routed_rows": T}
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+            "frac": gbs / PEAK_HBM_GBS, "traffic": _traffic("masked_gemm_mxfp4")}
     tf = flops / (ms * 1e-3) / 1e12
     return tf, ms, cfg, roof, {"masked_gemm_mxfp4": {"ms": ms, "TFLOP/s": tf, "GB/s": gbs}}, None
 
