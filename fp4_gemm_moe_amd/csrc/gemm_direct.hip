@@ -13,6 +13,9 @@
 //     E2M1 value times a UE4M3 value has at most 6 significant bits -- and
 //     multiplied on the BF16 matrix cores; alpha = g_A * g_B is applied in
 //     FP32).
+#include <mutex>
+#include <vector>
+
 #include "gemm_common.hpp"
 
 namespace hq {
@@ -72,21 +75,23 @@ __device__ __forceinline__ void load_slice(const uint8_t* row_codes, const uint8
   sc = kg < kgroups ? (int)row_sf[kg] : 127;
 }
 
-// NW waves split K (wave w takes K steps w, w + NW, ...), U steps per trip
-// so that U loads per operand are in flight per wave; the NW partial tiles
-// are summed through LDS.
-template <int FMT, int FM, int FN, int NW, int U>
-__global__ __launch_bounds__(NW * 64) void mx_gemm_direct(GemmArgs p) {
+// The block's NW = blockDim.x / 64 waves (at most NWMAX; at least 4 for the
+// grouped forms, whose tile table takes 256 threads) split K: wave w takes K
+// steps w, w + NW, ..., U steps per trip so that U loads per operand are in
+// flight per wave; the NW partial tiles are summed through LDS.
+template <int FMT, int FM, int FN, int NWMAX, int U>
+__global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
-  __shared__ v4f red[NW - 1][FM * FN][64];
+  __shared__ v4f red[NWMAX - 1][FM * FN][64];
+  const int NW = (int)(blockDim.x >> 6);
 
   const int G = p.num_groups;
   const int NT = (int)((p.n + TN - 1) / TN);
   const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
   int total_gm;
   if (p.form == kUniform) total_gm = G * mt_per;
-  else total_gm = build_tile_table<NW * 64>(p, TM, tt);
+  else total_gm = build_tile_table<256>(p, TM, tt);
   const int total = total_gm * NT;
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -160,7 +165,6 @@ __global__ __launch_bounds__(NW * 64) void mx_gemm_direct(GemmArgs p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           v4f v = acc[fm][fn];
-#pragma unroll
           for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           const int64_t n = n0 + fn * 16 + 4 * q;
           if (m < tr.row_end && n < p.n)
@@ -196,18 +200,19 @@ __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8
   return s;
 }
 
-template <int FM, int FN, int NW, int U>
-__global__ __launch_bounds__(NW * 64) void nv_gemm_direct(GemmArgs p) {
+template <int FM, int FN, int NWMAX, int U>
+__global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
-  __shared__ v4f red[NW - 1][FM * FN][64];
+  __shared__ v4f red[NWMAX - 1][FM * FN][64];
+  const int NW = (int)(blockDim.x >> 6);       // as for mx_gemm_direct
 
   const int G = p.num_groups;
   const int NT = (int)((p.n + TN - 1) / TN);
   const int mt_per = (int)((p.slot_rows + TM - 1) / TM);
   int total_gm;
   if (p.form == kUniform) total_gm = G * mt_per;
-  else total_gm = build_tile_table<NW * 64>(p, TM, tt);
+  else total_gm = build_tile_table<256>(p, TM, tt);
   const int total = total_gm * NT;
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -297,7 +302,6 @@ __global__ __launch_bounds__(NW * 64) void nv_gemm_direct(GemmArgs p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           v4f v = acc[fm][fn];
-#pragma unroll
           for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           v = v * alpha;
           const int64_t n = n0 + fn * 16 + 4 * q;
@@ -309,14 +313,54 @@ __global__ __launch_bounds__(NW * 64) void nv_gemm_direct(GemmArgs p) {
   }
 }
 
-template <class K>
-hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int TN,
-                         const DeviceInfo& dev, int threads = kThreads) {
+// Resident blocks per CU of `fn` at `threads` threads (the runtime's
+// occupancy calculator, cached per kernel and block size).
+int blocks_per_cu(const void* fn, int threads) {
+  struct Entry {
+    const void* fn;
+    int threads, blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.threads == threads) return e.blocks;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) != hipSuccess || nb < 1) nb = 1;
+  cache.push_back(Entry{fn, threads, nb});
+  return nb;
+}
+
+int64_t tile_count(const GemmArgs& p, int TM, int TN) {
   const int64_t NT = (p.n + TN - 1) / TN;
   int64_t gm_upper;
   if (p.form == kContiguous) gm_upper = (p.m_rows + TM - 1) / TM + p.num_groups;
   else gm_upper = (int64_t)p.num_groups * ((p.slot_rows + TM - 1) / TM);
-  int64_t tiles = gm_upper * NT;
+  return gm_upper * NT;
+}
+
+// Waves per block for a skinny (one-fragment) tile, whose weights stream
+// once: the most waves, up to NWMAX and the K steps, for which every tile
+// has a resident block at once (a second, partial round of blocks would
+// nearly double the time).  Grouped forms need at least 4 waves.
+template <class K>
+int skinny_waves(K kernel, int nwmax, const GemmArgs& p, int TM, int TN, const DeviceInfo& dev) {
+  const int64_t tiles = tile_count(p, TM, TN);
+  int cus = dev.num_cus;
+  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+  const int64_t ksteps = (p.k / 32 + 3) / 4;
+  const int lo = p.form == kUniform ? 1 : 4;
+  int hi = nwmax;
+  if (ksteps < hi) hi = ksteps > lo ? (int)ksteps : lo;
+  for (int nw = hi; nw > lo; --nw)
+    if ((int64_t)blocks_per_cu((const void*)kernel, nw * 64) * cus >= tiles) return nw;
+  return lo;
+}
+
+template <class K>
+hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int TN,
+                         const DeviceInfo& dev, int threads = kThreads) {
+  const int64_t tiles = tile_count(p, TM, TN);
   int cus = dev.num_cus;
   if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
   int64_t grid = (int64_t)cus * 8;
@@ -332,19 +376,32 @@ hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int
 hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
   const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
   const int fm = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
+  // one 16-row fragment (skinny M): for MX the wave count follows the tile
+  // count; NVFP4's decode keeps more registers live, so it keeps 8 waves
+  // (512-thread bounds) unless there are fewer tiles than CUs (measured)
   if (p.mode == kNVFP4) {
-    if (fm == 1) return launch_direct(s, nv_gemm_direct<1, 2, 8, 2>, p, 16, 32, dev, 512);
+    if (fm == 1) {
+      int cus = dev.num_cus;
+      if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+      if (tile_count(p, 16, 32) < cus && p.k >= 16 * 128)
+        return launch_direct(s, nv_gemm_direct<1, 2, 16, 2>, p, 16, 32, dev, 1024);
+      return launch_direct(s, nv_gemm_direct<1, 2, 8, 2>, p, 16, 32, dev, 512);
+    }
     if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
     return launch_direct(s, nv_gemm_direct<4, 2, 4, 1>, p, 64, 32, dev);
   }
-  // one 16-row fragment (skinny M): weights stream once, so 8 waves x 4
-  // steps of loads in flight per workgroup
   if (p.mode == kMXFP8) {
-    if (fm == 1) return launch_direct(s, mx_gemm_direct<0, 1, 1, 8, 4>, p, 16, 16, dev, 512);
+    if (fm == 1) {
+      auto k = mx_gemm_direct<0, 1, 1, 16, 4>;
+      return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
+    }
     if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2, 4, 2>, p, 32, 32, dev);
     return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2>, p, 64, 64, dev);
   }
-  if (fm == 1) return launch_direct(s, mx_gemm_direct<4, 1, 1, 8, 4>, p, 16, 16, dev, 512);
+  if (fm == 1) {
+    auto k = mx_gemm_direct<4, 1, 1, 16, 4>;
+    return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
+  }
   if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2, 4, 2>, p, 32, 32, dev);
   return launch_direct(s, mx_gemm_direct<4, 4, 4, 4, 2>, p, 64, 64, dev);
 }

@@ -23,12 +23,13 @@ struct OpMax {
   __device__ int operator()(int a, int b) const { return a > b ? a : b; }
 };
 
-// In-place inclusive scan of s[0, n) (n <= 1024) by a block of NT threads
-// (a multiple of 64, at most 1024).  Each thread scans 1024 / NT consecutive
-// entries, waves scan their thread totals with lane shuffles, and the wave
-// totals are combined through LDS.  `op` must be associative with `identity`
-// neutral.  Returns the scan's last value to every thread.  Must be reached
-// by all threads.
+// In-place inclusive scan of s[0, n) (n <= 1024) by the first NT threads of
+// the block (NT a multiple of 64, at most 1024); threads past NT only meet
+// the barriers.  Each scanning thread takes 1024 / NT consecutive entries,
+// waves scan their thread totals with lane shuffles, and the wave totals are
+// combined through LDS.  `op` must be associative with `identity` neutral.
+// Returns the scan's last value to every thread.  Must be reached by all
+// threads.
 template <int NT, class Op>
 __device__ int block_scan_1024(int* s, int n, Op op, int identity) {
   static_assert(NT % 64 == 0 && NT >= 64 && NT <= 1024, "block of whole waves, at most 1024 threads");
@@ -48,7 +49,7 @@ __device__ int block_scan_1024(int* s, int n, Op op, int identity) {
     int y = __shfl_up(x, off, 64);
     if (lane >= off) x = op(x, y);
   }
-  if (lane == 63) wsum[w] = x;
+  if (lane == 63 && w < NW) wsum[w] = x;     // threads past NT hold no entries
   __syncthreads();
   int prefix = identity, total = identity;
 #pragma unroll
