@@ -35,6 +35,8 @@
 // Requirements (checked by the dispatcher): K % 128 == 0 (FP8) or
 // K % 256 == 0 (FP4); scale pointers 4-byte aligned; lda * 256 < 2^31;
 // n * 512 < 2^31.
+#include <mutex>
+
 #include "gemm_common.hpp"
 
 namespace hq {
@@ -194,13 +196,24 @@ __device__ int build_tiled_table(const GemmArgs& p, TiledTable& t, int& n_heavy)
 // the byte bases / extents of its operands.
 struct Tile {
   int g;
+  int nk, slice;                 // K steps of this tile (range), K-split slice
   int64_t row0, row_end, n0;
   const uint8_t *a, *b, *sa, *sb;
   int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
 };
 
+template <int FMT>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& tt, int total_gm,
-                                          int n_heavy, int NT, int mt_per, int t) {
+                                          int n_heavy, int NT, int mt_per, int nk, int t) {
+  // K split: units are numbered slice-major, so that neighbouring units of
+  // one slice share operand rows as without a split
+  const int S = p.ksplit > 1 ? p.ksplit : 1;
+  int slice = 0;
+  if (S > 1) {
+    const int per_slice = total_gm * NT;
+    slice = t / per_slice;
+    t -= slice * per_slice;
+  }
   // blocks of 4 m-tiles x all n-tiles, walked n-major inside the block so 32
   // consecutive tiles = 4 m x 8 n
   const int blk = t / (4 * NT);
@@ -232,21 +245,27 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
   }
   Tile tl;
   tl.g = (int)ufirst((uint32_t)g);
+  // this slice's K steps [k0, k1) of the nk steps
+  const int k0 = (int)((int64_t)slice * nk / S), k1 = (int)((int64_t)(slice + 1) * nk / S);
+  tl.slice = (int)ufirst((uint32_t)slice);
+  tl.nk = (int)ufirst((uint32_t)(k1 - k0));
+  const int64_t kb = (int64_t)ufirst((uint32_t)k0) * SROW, ksb = (int64_t)ufirst((uint32_t)k0) * Cfg<FMT>::SB;
   tl.row0 = ufirst64(row0);
   tl.row_end = ufirst64(row_end);
   tl.n0 = (int64_t)nt * BN;
   const int64_t brow0 = (int64_t)tl.g * p.n + tl.n0;          // first weight row
   const int64_t brows = (int64_t)p.num_groups * p.n;
-  tl.a = uniform_ptr(p.a + tl.row0 * p.lda);
-  tl.b = uniform_ptr(p.b + brow0 * p.lda);
-  tl.sa = uniform_ptr(p.sfa + tl.row0 * p.ldsf);
-  tl.sb = uniform_ptr(p.sfb + brow0 * p.ldsf);
+  tl.a = uniform_ptr(p.a + tl.row0 * p.lda + kb);
+  tl.b = uniform_ptr(p.b + brow0 * p.lda + kb);
+  tl.sa = uniform_ptr(p.sfa + tl.row0 * p.ldsf + ksb);
+  tl.sb = uniform_ptr(p.sfb + brow0 * p.ldsf + ksb);
   // A rows past the tile's valid rows (the next group's, or a masked slot's
-  // padding) are not fetched: the bounded loads fill them with zeros
-  tl.a_bytes = (tl.row_end - tl.row0) * p.lda;
-  tl.b_bytes = (brows - brow0) * p.lda;
-  tl.sa_bytes = (tl.row_end - tl.row0) * p.ldsf;
-  tl.sb_bytes = (brows - brow0) * p.ldsf;
+  // padding) are not fetched: the bounded loads fill them with zeros.
+  // Extents count from the slice's first K byte.
+  tl.a_bytes = (tl.row_end - tl.row0) * p.lda - kb;
+  tl.b_bytes = (brows - brow0) * p.lda - kb;
+  tl.sa_bytes = (tl.row_end - tl.row0) * p.ldsf - ksb;
+  tl.sb_bytes = (brows - brow0) * p.ldsf - ksb;
   return tl;
 }
 
@@ -335,7 +354,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
-template <int FMT>
+// SPLIT: the launch has a K split (p.ksplit > 1) and the epilogue writes
+// FP32 partial tiles instead of the BF16 output (a separate instantiation, so
+// that the second epilogue costs the single-pass kernel no registers).
+template <int FMT, bool SPLIT>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
   constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
@@ -349,14 +371,16 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   int total_gm, n_heavy = 0;
   if (p.form == kUniform) total_gm = G0 * mt_per;
   else total_gm = build_tiled_table<FMT>(p, tt, n_heavy);
-  const int total = total_gm * NT;
+  const int total = total_gm * NT * (p.ksplit > 1 ? p.ksplit : 1);
 
   const int tid = threadIdx.x;
   const int w = ufirst(tid >> 6);                           // wave index (uniform)
   const int lane = tid & 63;
   const int wm = w / WGN, wn = w % WGN;                     // wave grid (M x N)
   const int h = lane >> 5, r32 = lane & 31;
-  const int nk = (int)(p.lda / SROW);
+  const int nk = (int)(p.lda / SROW);          // K steps of a whole row
+  // more than one K step in every tile (K-split ranges have at least two)
+  const bool multi = p.ksplit > 1 || nk > 1;
 
   // XCD-aware order: workgroup b runs on XCD b % 8; inside a round of
   // gridDim tiles XCD x owns a contiguous run of tiles.  Rounds alternate
@@ -558,12 +582,12 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
   };
 
-  Tile tl = make_tile(p, tt, total_gm, n_heavy, NT, mt_per, t);
+  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t);
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
   issue<FMT>(tl, lo, 0, smem_lds, w);
-  if (nk > 1) {
+  if (multi) {
     issue<FMT>(tl, lo, 1, smem_lds + C::STAGE, w);
     wait_vm<C::OPS>();
   } else {
@@ -585,7 +609,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     // previous tile's stores; step k >= 1 issues step k + 1 into the stage
     // step k - 1 used.
     auto nothing = []() {};
-    if (nk > 1) {
+    if (multi) {
       // step 0: step 1's loads were issued with step 0's, before the previous
       // tile's stores, which stay in flight
       step(smem + st * C::STAGE, nothing);
@@ -596,7 +620,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       bar();
       st ^= 1;
     }
-    for (int k = 1; k + 1 < nk; ++k) {
+    for (int k = 1; k + 1 < tl.nk; ++k) {
       const uint32_t nxt = smem_lds + (st ^ 1) * C::STAGE;
       step(smem + st * C::STAGE, [&]() { issue<FMT>(tl, lo, k + 1, nxt, w); });
       __builtin_amdgcn_sched_barrier(0);
@@ -609,72 +633,100 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     const bool has_next = t_next < total;
     Tile tn = tl;
     if (has_next) {
-      tn = make_tile(p, tt, total_gm, n_heavy, NT, mt_per, t_next);
+      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next);
       issue<FMT>(tn, lo, 0, smem_lds + (st ^ 1) * C::STAGE, w);
     }
     step(smem + st * C::STAGE, []() {});
     pin();
     bar();                            // stage `st` is free
-    if (has_next && nk > 1) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
+    if (has_next && multi) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
 
-    // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
-    // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
-    // in register 4b + r, i.e. out[m = l%32][n = 8b + 4(l/32) + r].  Lanes l
-    // and l^32 swap one 4-column quad so each lane owns 8 consecutive
-    // columns: lane group 0 stores columns 8b..8b+7 for b = 0, 2 and lane
-    // group 1 for b = 1, 3.
-    const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tl.row0 * p.n));
-    const uint32_t obytes = ufirst((uint32_t)((tl.row_end - tl.row0) * p.n * 2));
-    const __amdgpu_buffer_rsrc_t orsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
-    const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
-    const float alpha = FMT == kNV ? p.alpha[tl.g] : 1.0f;   // NVFP4: g_A * g_B per group
+    if constexpr (SPLIT) {
+      // ---- K-split epilogue: this slice's FP32 partial tile to
+      // partial[slice][row][col], 16-byte buffer stores of 4 consecutive
+      // columns (lane l, register 4b + r holds fragment row l % 32, column
+      // 8b + 4(l/32) + r); rows past the tile end fall outside the
+      // descriptor, columns past n take the drop marker.
+      const uint8_t* pb = uniform_ptr(reinterpret_cast<const uint8_t*>(
+          p.partial + ((int64_t)tl.slice * p.m_rows + tl.row0) * p.n));
+      const uint32_t pbytes = ufirst((uint32_t)((tl.row_end - tl.row0) * p.n * 4));
+      const __amdgpu_buffer_rsrc_t prsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pb), (short)0, (int)pbytes, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      v4f bq[4];
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * b + 4 * h;
-        bq[b] = v4f{0.f, 0.f, 0.f, 0.f};
-        if (bias != nullptr && n < p.n) {
-          uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-          bq[b] = v4f{bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
+        for (int i = 0; i < FI; ++i) {
+          const int64_t mr = wm * WTM + i * 32 + r32;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * b + 4 * h;
+            const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 4) : 0x80000000u;
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u o = v4u{__float_as_uint(acc[i][j][4 * b]), __float_as_uint(acc[i][j][4 * b + 1]),
+                              __float_as_uint(acc[i][j][4 * b + 2]), __float_as_uint(acc[i][j][4 * b + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(o, prsrc, (int)off, 0, 0);
+          }
         }
-      }
+    } else {
+      // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
+      // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
+      // in register 4b + r, i.e. out[m = l%32][n = 8b + 4(l/32) + r].  Lanes l
+      // and l^32 swap one 4-column quad so each lane owns 8 consecutive
+      // columns: lane group 0 stores columns 8b..8b+7 for b = 0, 2 and lane
+      // group 1 for b = 1, 3.
+      const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tl.row0 * p.n));
+      const uint32_t obytes = ufirst((uint32_t)((tl.row_end - tl.row0) * p.n * 2));
+      const __amdgpu_buffer_rsrc_t orsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
+      const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
+      const float alpha = FMT == kNV ? p.alpha[tl.g] : 1.0f;   // NVFP4: g_A * g_B per group
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const int64_t mr = wm * WTM + i * 32 + r32;            // row within the tile
-        uint32_t pk[4][2];
+      for (int j = 0; j < FJ; ++j) {
+        v4f bq[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          float f[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            f[r] = FMT == kNV ? acc[i][j][4 * b + r] * alpha : acc[i][j][4 * b + r] + bq[b][r];
-          pk[b][0] = pack_bf16x2(f[0], f[1]);
-          pk[b][1] = pack_bf16x2(f[2], f[3]);
+          const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * b + 4 * h;
+          bq[b] = v4f{0.f, 0.f, 0.f, 0.f};
+          if (bias != nullptr && n < p.n) {
+            uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+            bq[b] = v4f{bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
-          const int bl = 2 * e, bh = 2 * e + 1;
-          // group 0 sends its b = 2e+1 quad and receives the partner's b = 2e
-          // quad; group 1 the other way round
-          uint32_t s0w = h == 0 ? pk[bh][0] : pk[bl][0];
-          uint32_t s1w = h == 0 ? pk[bh][1] : pk[bl][1];
-          uint32_t r0 = (uint32_t)__shfl_xor((int)s0w, 32, 64);
-          uint32_t r1 = (uint32_t)__shfl_xor((int)s1w, 32, 64);
-          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-          v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
-          const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * (h == 0 ? bl : bh);
-          const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
-          __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
+        for (int i = 0; i < FI; ++i) {
+          const int64_t mr = wm * WTM + i * 32 + r32;            // row within the tile
+          uint32_t pk[4][2];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float f[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              f[r] = FMT == kNV ? acc[i][j][4 * b + r] * alpha : acc[i][j][4 * b + r] + bq[b][r];
+            pk[b][0] = pack_bf16x2(f[0], f[1]);
+            pk[b][1] = pack_bf16x2(f[2], f[3]);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
+            const int bl = 2 * e, bh = 2 * e + 1;
+            // group 0 sends its b = 2e+1 quad and receives the partner's b = 2e
+            // quad; group 1 the other way round
+            uint32_t s0w = h == 0 ? pk[bh][0] : pk[bl][0];
+            uint32_t s1w = h == 0 ? pk[bh][1] : pk[bl][1];
+            uint32_t r0 = (uint32_t)__shfl_xor((int)s0w, 32, 64);
+            uint32_t r1 = (uint32_t)__shfl_xor((int)s1w, 32, 64);
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
+            const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * (h == 0 ? bl : bh);
+            const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
+          }
         }
       }
     }
     if (!has_next) break;
     // the next tile's step 0 was issued before its step 1 (nk > 1) and these
     // kStores stores
-    if (nk > 1) wait_vm<C::OPS + kStores>();
+    if (multi) wait_vm<C::OPS + kStores>();
     else wait_vm<kStores>();
     bar();
     t = t_next;
@@ -685,14 +737,79 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   }
 }
 
+// Sums the K-split partial tiles slice by slice, in slice order, and writes
+// the BF16 output with the bias (MX) or alpha (NVFP4) of the row's group:
+// the same arithmetic as the single-pass epilogue on the summed tile.  Block
+// b takes rows b, b + grid, ...; its threads walk the row's 4-column chunks
+// (n % 8 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
+  const int64_t plane = p.m_rows * p.n;          // floats per slice
+  const int64_t chunks = p.n / 4;
+  for (int64_t row = blockIdx.x; row < p.m_rows; row += gridDim.x) {
+    const int64_t g = row / p.slot_rows;
+    const float alpha = p.mode == kNVFP4 ? p.alpha[g] : 1.0f;
+    const uint16_t* bias = p.bias ? p.bias + g * p.n : nullptr;
+    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
+      const int64_t e = row * p.n + 4 * c;
+      v4f v = *reinterpret_cast<const v4f*>(p.partial + e);
+      for (int sl = 1; sl < p.ksplit; ++sl) v += *reinterpret_cast<const v4f*>(p.partial + sl * plane + e);
+      float f[4];
+      if (p.mode == kNVFP4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = v[r] * alpha;
+      } else if (bias != nullptr) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + 4 * c);
+        f[0] = v[0] + bf16_lo(bb.x);
+        f[1] = v[1] + bf16_hi(bb.x);
+        f[2] = v[2] + bf16_lo(bb.y);
+        f[3] = v[3] + bf16_hi(bb.y);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = v[r];
+      }
+      *reinterpret_cast<uint2*>(p.out + e) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    }
+  }
+}
+
+// The library's stream-ordered pool for K-split workspaces, one per device:
+// freed blocks stay in the pool (no release threshold), so a repeated shape
+// reuses its memory without returning to the driver.
+hipMemPool_t workspace_pool(int device) {
+  static std::mutex mu;
+  static hipMemPool_t pools[64] = {};
+  static bool failed[64] = {};
+  if (device < 0 || device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (pools[device] == nullptr && !failed[device]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = device;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+      failed[device] = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    pools[device] = pool;
+  }
+  return pools[device];
+}
+
 template <int FMT>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
   using C = Cfg<FMT>;
   const int smem = 2 * C::STAGE;
   static bool attr_set = false;   // per process; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT>,
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -703,12 +820,47 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   const int64_t tiles = gm_upper * NT;
   int cus = dev.num_cus;
   if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+
+  // K split where the tiles cannot fill half of the CUs (dense and batch
+  // forms): S slices of at least 4 K steps each, S * tiles <= CUs, at most 8.
+  GemmArgs q = p;
+  q.ksplit = 1;
+  q.partial = nullptr;
+  const int64_t nk = p.lda / SROW;
+  if (p.form == kUniform && tiles * 2 <= cus && nk >= 8 && p.n * 1024 < ((int64_t)1 << 31)) {
+    int64_t S = cus / tiles;
+    if (S > nk / 4) S = nk / 4;
+    if (S > 8) S = 8;
+    hipMemPool_t pool = S >= 2 ? workspace_pool(dev.device) : nullptr;
+    void* ws = nullptr;
+    if (pool != nullptr &&
+        hipMallocFromPoolAsync(&ws, (size_t)(S * p.m_rows * p.n * 4), pool, s) == hipSuccess) {
+      q.ksplit = (int32_t)S;
+      q.partial = static_cast<float*>(ws);
+    } else {
+      (void)hipGetLastError();        // no workspace: run unsplit
+    }
+  }
   int64_t grid = cus;
-  if (tiles < grid) grid = tiles;
+  if (tiles * q.ksplit < grid) grid = tiles * q.ksplit;
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((mx_gemm_tiled<FMT>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, p);
-  return hipGetLastError();
+  if (q.ksplit > 1)
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, true>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+  else
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, false>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+  hipError_t e = hipGetLastError();
+  if (q.ksplit > 1) {
+    if (e == hipSuccess) {
+      int64_t rgrid = (int64_t)cus * 4;
+      if (p.m_rows < rgrid) rgrid = p.m_rows;
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q);
+      e = hipGetLastError();
+    }
+    const hipError_t ef = hipFreeAsync(q.partial, s);
+    if (e == hipSuccess) e = ef;
+  }
+  return e;
 }
 
 }  // namespace

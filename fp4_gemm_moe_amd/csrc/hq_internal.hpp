@@ -40,6 +40,12 @@ struct GemmArgs {
   int32_t form;
   int32_t mode;
   int32_t cu_limit;
+  // K split (tiled kernel, uniform form only): ksplit > 1 slices the K steps
+  // of every tile into ksplit contiguous ranges; each range's FP32 partial
+  // tile goes to partial[slice][row][col] and a second kernel sums the slices
+  // in order and writes the BF16 output.  Set by the tiled launcher.
+  int32_t ksplit;
+  float* partial;
 };
 
 struct DeviceInfo {

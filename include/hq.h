@@ -12,9 +12,12 @@
  * Conventions shared by every call
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers (memory of the current HIP
- *    device).  The caller allocates and owns every buffer; the library never
- *    allocates, keeps no pointer after a call returns and never synchronises
- *    the host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    device).  The caller allocates and owns every buffer; the library keeps
+ *    no pointer after a call returns and never synchronises the host.  The
+ *    one allocation it makes is the FP32 workspace of a K-split dense or
+ *    batch GEMM (see hq_dense_gemm), taken from and returned to the
+ *    library's own per-device stream-ordered pool inside the call's stream
+ *    order.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and is stream-ordered, so a call may be captured into a graph.
  *  - BF16 values are passed as their uint16_t bit patterns.
  *  - Quantised operands are K-major and row-major:
@@ -103,6 +106,14 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x,
  * alpha (device float[1]) is required in NVFP4 mode and rejected otherwise.
  * Accumulation is FP32 on the matrix cores; the output is rounded once to
  * BF16 (nearest even).  cu_limit > 0 caps the compute units used (<= 0: all).
+ * When the output tiles cannot fill half of the compute units and K is long
+ * (at least 8 K steps of 128 bytes per row), K is split into 2..8 contiguous
+ * slices: each slice's FP32 partial products go to a workspace of
+ * slices * m * n floats (batch: batch * m rows), a second kernel adds the
+ * slices in order and applies bias / alpha, then rounds once to BF16.  The
+ * workspace comes from the library's stream-ordered pool; if it cannot be
+ * had, the call runs unsplit.  FP32 summation order (not the result's
+ * contract) then differs from an unsplit call.
  */
 hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
                         const uint8_t* sfa, const uint8_t* b,

@@ -107,6 +107,62 @@ def test_dense_random_small(mode):
         U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"{mode} {m}x{n}x{k}")
 
 
+# Few tiles and a long K: the tiled kernel splits K into slices (uneven here)
+# whose FP32 partial tiles a second kernel sums before the BF16 rounding.
+K_SPLIT_SHAPES = {"mxfp8": (300, 520, 8576), "mxfp4": (200, 264, 8448), "nvfp4": (130, 512, 8448)}
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+def test_k_split_integer_exact(mode):
+    dev = U.require_gpu()
+    m, n, k = K_SPLIT_SHAPES[mode]
+    U.banner(f"k-split int-exact {mode} m={m} n={n} k={k}")
+    rng = np.random.default_rng(k + m)
+    av, a, sfa = _int_operand(rng, m, k, mode, [-1, 0, 1])
+    bv, b, sfb = _int_operand(rng, n, k, mode, [-1, 0, 1])
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None)
+    want = F.bf16_round((av @ bv.T).astype(np.float64))
+    assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+def test_k_split_random(mode):
+    dev = U.require_gpu()
+    m, n, k = K_SPLIT_SHAPES[mode]
+    U.banner(f"k-split random {mode} m={m} n={n} k={k}")
+    rng = np.random.default_rng(7 * k + n)
+    a, sfa, ga = _quant(synth.normal_bf16(rng, (m, k)), mode)
+    b, sfb, gb = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
+    alpha = None if ga is None else np.float32(ga * gb)
+    bias = synth.normal_bf16(rng, (n,), 0.1) if mode == "mxfp8" else None
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha)
+    want = G.dense_gemm(mode, a, sfa, b, sfb, bias, alpha)
+    U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"k-split {mode}")
+
+
+def test_k_split_batch_with_bias():
+    """Batch form: each batch's rows take its own weights and bias after the
+    slices are summed."""
+    dev = U.require_gpu()
+    Bn, m, n, k = 3, 100, 128, 4096
+    rng = np.random.default_rng(31)
+    a, sfa = Q.mx_quant_bf16(synth.normal_bf16(rng, (Bn * m, k)), "mxfp8")
+    b, sfb = Q.mx_quant_bf16(synth.normal_bf16(rng, (Bn * n, k), 0.05), "mxfp8")
+    bias = synth.normal_bf16(rng, (Bn, n), 0.1)
+    out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
+    U.banner("k-split batch mxfp8")
+    hq.hq_batch_gemm("mxfp8", U.dev_u8(a, dev).view(Bn, m, k), U.dev_u8(sfa, dev).view(Bn, m, -1),
+                     U.dev_u8(b, dev).view(Bn, n, k), U.dev_u8(sfb, dev).view(Bn, n, -1), out,
+                     bias=U.dev_bf16(bias, dev))
+    torch.cuda.synchronize()
+    want = G.batch_gemm("mxfp8", a.reshape(Bn, m, k), sfa.reshape(Bn, m, -1), b.reshape(Bn, n, k),
+                        sfb.reshape(Bn, n, -1), bias=bias)
+    got = U.host_bits(out)
+    for i in range(Bn):
+        U.assert_gemm_close(got[i], want[i], U.deq("mxfp8", a[i * m:(i + 1) * m], sfa[i * m:(i + 1) * m]),
+                            U.deq("mxfp8", b[i * n:(i + 1) * n], sfb[i * n:(i + 1) * n]), what=f"batch {i}")
+
+
 def test_config0_dense_mxfp8_256_with_gpu_quant():
     """256^3 MXFP8, seed 0: quantised on the GPU (bit-exact to the oracle),
     then the GEMM within tolerance."""
