@@ -75,11 +75,33 @@ __device__ __forceinline__ void load_slice(const uint8_t* row_codes, const uint8
   sc = kg < kgroups ? (int)row_sf[kg] : 127;
 }
 
+// Codes only of the same slice (zeros when !in); the scale bytes come from
+// one 8-byte load per K-step pair instead.
+template <int FMT>
+__device__ __forceinline__ v8i load_codes(const uint8_t* row_codes, int t, int q, bool in) {
+  if (FMT == 0) {
+    const uint8_t* base = row_codes + (int64_t)t * 128 + 16 * q;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (in) {
+      lo = *reinterpret_cast<const uint4*>(base);
+      hi = *reinterpret_cast<const uint4*>(base + 64);
+    }
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  uint4 lo = make_uint4(0, 0, 0, 0);
+  if (in) lo = *reinterpret_cast<const uint4*>(row_codes + (int64_t)(t * 4 + q) * 16);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+}
+
 // The block's NW = blockDim.x / 64 waves (at most NWMAX; at least 4 for the
 // grouped forms, whose tile table takes 256 threads) split K: wave w takes K
 // steps w, w + NW, ..., U steps per trip so that U loads per operand are in
 // flight per wave; the NW partial tiles are summed through LDS.
-template <int FMT, int FM, int FN, int NWMAX, int U>
+// SC8 (K % 256 == 0, scale rows 8-byte aligned): the K steps go to the waves
+// in pairs (pair j = steps 2j, 2j + 1, wave w takes pairs w, w + NW, ...) and
+// a lane reads the 8 scale bytes of a pair in one load (its lane group's
+// bytes are q and 4 + q) instead of one byte per step.
+template <int FMT, int FM, int FN, int NWMAX, int U, bool SC8 = false>
 __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
@@ -131,23 +153,62 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int t = w; t < ksteps; t += NW * U) {
-      v8i af[U][FM], bf[U][FN];
-      int sa[U][FM], sb[U][FN];
+    if constexpr (SC8) {
+      static_assert(U % 2 == 0, "whole pairs per trip");
+      const int npairs = ksteps >> 1;
+      for (int p0 = w; p0 < npairs; p0 += NW * (U / 2)) {
+        v8i af[U][FM], bf[U][FN];
+        int sa[U][FM], sb[U][FN];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+        for (int v = 0; v < U / 2; ++v) {
+          const int pp = p0 + NW * v;
+          const bool in = pp < npairs;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) load_slice<FMT>(arow[fm], asf[fm], t + NW * u, q, kgroups, af[u][fm], sa[u][fm]);
+          for (int fm = 0; fm < FM; ++fm) {
+            const uint2 s8 = in ? *reinterpret_cast<const uint2*>(asf[fm] + 8 * (int64_t)pp) : make_uint2(0u, 0u);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) load_slice<FMT>(brow[fn], bsf[fn], t + NW * u, q, kgroups, bf[u][fn], sb[u][fn]);
+            for (int e = 0; e < 2; ++e) {
+              af[2 * v + e][fm] = load_codes<FMT>(arow[fm], 2 * pp + e, q, in);
+              sa[2 * v + e][fm] = (int)(((e == 0 ? s8.x : s8.y) >> (8 * q)) & 0xFFu);
+            }
+          }
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const uint2 s8 = in ? *reinterpret_cast<const uint2*>(bsf[fn] + 8 * (int64_t)pp) : make_uint2(0u, 0u);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              bf[2 * v + e][fn] = load_codes<FMT>(brow[fn], 2 * pp + e, q, in);
+              sb[2 * v + e][fn] = (int)(((e == 0 ? s8.x : s8.y) >> (8 * q)) & 0xFFu);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = mfma_scaled<FMT>(bf[u][fn], af[u][fm], acc[fm][fn], sb[u][fn], sa[u][fm]);
       }
+    } else {
+      for (int t = w; t < ksteps; t += NW * U) {
+        v8i af[U][FM], bf[U][FN];
+        int sa[U][FM], sb[U][FN];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm) load_slice<FMT>(arow[fm], asf[fm], t + NW * u, q, kgroups, af[u][fm], sa[u][fm]);
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = mfma_scaled<FMT>(bf[u][fn], af[u][fm], acc[fm][fn], sb[u][fn], sa[u][fm]);
+          for (int fn = 0; fn < FN; ++fn) load_slice<FMT>(brow[fn], bsf[fn], t + NW * u, q, kgroups, bf[u][fn], sb[u][fn]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = mfma_scaled<FMT>(bf[u][fn], af[u][fm], acc[fm][fn], sb[u][fn], sa[u][fm]);
+      }
     }
 
     if (w > 0) {
@@ -390,8 +451,15 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
     if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
     return launch_direct(s, nv_gemm_direct<4, 2, 4, 1>, p, 64, 32, dev);
   }
+  // scale rows in whole, 8-byte aligned pairs of K steps
+  const bool sc8 = p.k % 256 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 7) == 0;
   if (p.mode == kMXFP8) {
     if (fm == 1) {
+      if (sc8) {
+        auto k = mx_gemm_direct<0, 1, 1, 16, 4, true>;
+        return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
+      }
       auto k = mx_gemm_direct<0, 1, 1, 16, 4>;
       return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
     }
@@ -399,6 +467,10 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
     return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2>, p, 64, 64, dev);
   }
   if (fm == 1) {
+    if (sc8) {
+      auto k = mx_gemm_direct<4, 1, 1, 16, 4, true>;
+      return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
+    }
     auto k = mx_gemm_direct<4, 1, 1, 16, 4>;
     return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
   }
