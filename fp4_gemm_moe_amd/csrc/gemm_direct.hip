@@ -261,7 +261,10 @@ __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8
   return s;
 }
 
-template <int FM, int FN, int NWMAX, int U>
+// SC16 (K % 256 == 0, scale rows 16-byte aligned): K steps in pairs as for
+// mx_gemm_direct; a lane reads the 16 scale bytes of a pair in one load and
+// decodes its two UE4M3 bytes per step with the hardware FP8 conversion.
+template <int FM, int FN, int NWMAX, int U, bool SC16 = false>
 __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
@@ -311,16 +314,56 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int t0 = w; t0 < ksteps; t0 += NW * U) {
+    // trips: U steps each; with SC16 the steps of a trip are U / 2 pairs
+    const int trip_stride = SC16 ? NW * (U / 2) : NW * U;
+    const int trips_end = SC16 ? (ksteps >> 1) : ksteps;
+    for (int t0 = w; t0 < trips_end; t0 += trip_stride) {
       NvSlice as[U][FM], bs[U][FN];
+      if constexpr (SC16) {
+        static_assert(U % 2 == 0, "whole pairs per trip");
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        auto pair_slices = [&](const uint8_t* rc, const uint8_t* rs, int pp, bool in, NvSlice* out2) {
+          const uint4 s16 = in ? *reinterpret_cast<const uint4*>(rs + 16 * (int64_t)pp) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kb = (t0 + NW * u) * 4 + q;
-        const bool kin = kb < kblocks;
+          for (int e = 0; e < 2; ++e) {
+            const int kb = (2 * pp + e) * 4 + q;
+            out2[e].codes = in ? *reinterpret_cast<const uint4*>(rc + (int64_t)kb * 16) : make_uint4(0, 0, 0, 0);
+            // bytes 8e + 2q and 8e + 2q + 1 of the pair: dword 2e + q/2, half q & 1
+            const uint32_t d = e == 0 ? (q < 2 ? s16.x : s16.y) : (q < 2 ? s16.z : s16.w);
+            const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((d >> (16 * (q & 1))) & 0x7F7Fu, 1.0f, false);
+            out2[e].s0 = f[0];
+            out2[e].s1 = f[1];
+          }
+        };
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) as[u][fm] = nv_load(arow[fm], asf[fm], kb, kin);
+        for (int v = 0; v < U / 2; ++v) {
+          const int pp = t0 + NW * v;
+          const bool in = pp < (ksteps >> 1);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bs[u][fn] = nv_load(brow[fn], bsf[fn], kb, kin);
+          for (int fm = 0; fm < FM; ++fm) {
+            NvSlice two[2];
+            pair_slices(arow[fm], asf[fm], pp, in, two);
+            as[2 * v][fm] = two[0];
+            as[2 * v + 1][fm] = two[1];
+          }
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            NvSlice two[2];
+            pair_slices(brow[fn], bsf[fn], pp, in, two);
+            bs[2 * v][fn] = two[0];
+            bs[2 * v + 1][fn] = two[1];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kb = (t0 + NW * u) * 4 + q;
+          const bool kin = kb < kblocks;
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) as[u][fm] = nv_load(arow[fm], asf[fm], kb, kin);
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) bs[u][fn] = nv_load(brow[fn], bsf[fn], kb, kin);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -444,8 +487,14 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
     if (fm == 1) {
       int cus = dev.num_cus;
       if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
-      if (tile_count(p, 16, 32) < cus && p.k >= 16 * 128)
-        return launch_direct(s, nv_gemm_direct<1, 2, 16, 2>, p, 16, 32, dev, 1024);
+      const bool few = tile_count(p, 16, 32) < cus && p.k >= 16 * 128;
+      const bool sc16 = p.k % 256 == 0 &&
+                        ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 15) == 0;
+      if (sc16) {
+        if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2, true>, p, 16, 32, dev, 1024);
+        return launch_direct(s, nv_gemm_direct<1, 2, 8, 2, true>, p, 16, 32, dev, 512);
+      }
+      if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2>, p, 16, 32, dev, 1024);
       return launch_direct(s, nv_gemm_direct<1, 2, 8, 2>, p, 16, 32, dev, 512);
     }
     if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
