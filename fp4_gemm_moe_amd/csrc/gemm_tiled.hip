@@ -35,6 +35,7 @@
 // Requirements (checked by the dispatcher): K % 128 == 0 (FP8) or
 // K % 256 == 0 (FP4); scale pointers 4-byte aligned; lda * 256 < 2^31;
 // n * 512 < 2^31.
+#include <atomic>
 #include <mutex>
 
 #include "gemm_common.hpp"
@@ -803,15 +804,18 @@ template <int FMT>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
   using C = Cfg<FMT>;
   const int smem = 2 * C::STAGE;
-  static bool attr_set = false;   // per process; the attribute is per function
-  if (!attr_set) {
+  // the dynamic-LDS attribute, once per device and instantiation (setting it
+  // twice from racing threads is harmless)
+  static std::atomic<bool> attr_set[64];
+  const bool cached = dev.device >= 0 && dev.device < 64;
+  if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               smem);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (cached) attr_set[dev.device].store(true, std::memory_order_release);
   }
   const int64_t NT = (p.n + BN - 1) / BN;
   int64_t gm_upper;

@@ -163,6 +163,29 @@ def test_k_split_batch_with_bias():
                             U.deq("mxfp8", b[i * n:(i + 1) * n], sfb[i * n:(i + 1) * n]), what=f"batch {i}")
 
 
+def test_k_split_batch_nvfp4_alpha():
+    """Batch NVFP4 with a different alpha per item: the slice sum of each row is
+    scaled by its own item's alpha."""
+    dev = U.require_gpu()
+    Bn, m, n, k = 2, 96, 256, 8192
+    rng = np.random.default_rng(32)
+    a, sfa, ga = _quant(synth.normal_bf16(rng, (Bn * m, k)), "nvfp4")
+    b, sfb, gb = _quant(synth.normal_bf16(rng, (Bn * n, k), 0.05), "nvfp4")
+    alpha = np.array([ga * gb, np.float32(3.0) * ga * gb], np.float32)
+    out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
+    U.banner("k-split batch nvfp4")
+    hq.hq_batch_gemm("nvfp4", U.dev_u8(a, dev).view(Bn, m, -1), U.dev_u8(sfa, dev).view(Bn, m, -1),
+                     U.dev_u8(b, dev).view(Bn, n, -1), U.dev_u8(sfb, dev).view(Bn, n, -1), out,
+                     alpha=torch.from_numpy(alpha).to(dev))
+    torch.cuda.synchronize()
+    got = U.host_bits(out)
+    for i in range(Bn):
+        rows, cols = slice(i * m, (i + 1) * m), slice(i * n, (i + 1) * n)
+        want = G.dense_gemm("nvfp4", a[rows], sfa[rows], b[cols], sfb[cols], alpha=alpha[i])
+        U.assert_gemm_close(got[i], want, U.deq("nvfp4", a[rows], sfa[rows]), U.deq("nvfp4", b[cols], sfb[cols]),
+                            alpha[i], f"batch {i}")
+
+
 def test_config0_dense_mxfp8_256_with_gpu_quant():
     """256^3 MXFP8, seed 0: quantised on the GPU (bit-exact to the oracle),
     then the GEMM within tolerance."""
