@@ -9,7 +9,7 @@ imports nothing from the product path: the two share no code.
 Sources (the pages are cited by title and section):
   * HALOps "GEMM" API page: sections batch_gemm, dense_gemm,
     fused_swiglu_quant, group_contiguous_gemm, group_masked_gemm,
-    group_wise_quant.
+    group_wise_quant, prefill_permute_to_masked_gemm.
   * flashrt/fp4-gemm kernel page: function list and Notes (NVFP4 A4W4).
   * cuDNN Frontend "Grouped GEMM + dGLU (SM100)": Step 1 equation (the
     dequantize-dequantize definition of the block-scaled grouped GEMM) and
