@@ -19,6 +19,8 @@ __all__ = [
     "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
+    "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
+    "HQ_SCALE_BROADCAST", "HQ_SCALE_DIRECT",
     "hq_last_error", "library_path", "load", "EXPORTED_SYMBOLS",
     "quantize", "group_size", "code_cols",
 ]
@@ -27,6 +29,8 @@ HQ_MXFP8 = 0
 HQ_MXFP4 = 1
 HQ_NVFP4 = 2
 HQ_GS_INPUT = 1
+HQ_SCALE_BROADCAST = 0
+HQ_SCALE_DIRECT = 1
 
 MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
          "w8a8-mxfp8": HQ_MXFP8, "w4a4-mxfp4": HQ_MXFP4, "w4a4-nvfp4": HQ_NVFP4}
@@ -34,6 +38,7 @@ MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
 EXPORTED_SYMBOLS = (
     "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
+    "hq_prefill_permute_to_masked_gemm",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +71,8 @@ _SIGS = {
                               _I64, _I64, _I32], _I32),
     "hq_fused_swiglu_quant": ([_VP, _I32, _VP, _I64, _I64, _I32, _VP, _I64, _VP, _VP, _VP,
                                _VP, _VP], _I32),
+    "hq_prefill_permute_to_masked_gemm": ([_VP, _VP, _I64, _I64, _I64, _VP, _I32, _VP, _I32, _I32,
+                                           _I64, _VP, _VP, _VP, _VP], _I32),
 }
 
 
@@ -226,6 +233,55 @@ def hq_fused_swiglu_quant(mode, x, q, sf, num_groups, group_end=None, slot_rows=
     _check(load().hq_fused_swiglu_quant(_stream(x), mode, _p(x), rows, h, num_groups,
                                         _p(group_end), slot_rows, _p(valid), _p(q), _p(sf),
                                         _p(global_scale), _p(y_debug)))
+
+
+def hq_prefill_permute_to_masked_gemm(x, scale, topk_ids, num_local_experts, max_token_num,
+                                      permute_x, out_scale, indice_map, token_nums, hidden=None):
+    """Token permute into the masked-GEMM layout, in place: x [T, row_bytes
+    as any dtype] rows go to permute_x [E * max_token_num, ...] by topk_ids
+    [T, topk] int64; scale is int32 [T, hidden/512] (broadcast mode) or uint8
+    [T, hidden/32] (direct mode); out_scale uint8 [E, max_token_num,
+    hidden/32]; indice_map int32 [T, topk]; token_nums int32 [E]."""
+    T = x.shape[0]
+    row_bytes = x[0].numel() * x.element_size() if T > 0 else x.shape[-1] * x.element_size()
+    if scale.dtype == torch.int32:
+        mode, hidden = HQ_SCALE_BROADCAST, (scale.shape[-1] * 512 if hidden is None else hidden)
+    elif scale.dtype == torch.uint8:
+        mode, hidden = HQ_SCALE_DIRECT, (scale.shape[-1] * 32 if hidden is None else hidden)
+    else:
+        raise ValueError("scale must be int32 (broadcast mode) or uint8 (direct mode)")
+    topk = topk_ids.shape[-1]
+    E, M = int(num_local_experts), int(max_token_num)
+    for t, name in ((x, "x"), (permute_x, "permute_x")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if permute_x.numel() * permute_x.element_size() != E * M * row_bytes:
+        raise ValueError("permute_x must hold num_local_experts * max_token_num rows of x's width")
+    _need(scale, "scale", scale.dtype, T * (hidden // (512 if mode == HQ_SCALE_BROADCAST else 32)))
+    _need(topk_ids, "topk_ids", torch.int64, T * topk)
+    _need(out_scale, "out_scale", torch.uint8, E * M * (hidden // 32))
+    _need(indice_map, "indice_map", torch.int32, T * topk)
+    _need(token_nums, "token_nums", torch.int32, E)
+    _check(load().hq_prefill_permute_to_masked_gemm(
+        _stream(x), _p(x), T, row_bytes, hidden, _p(scale), mode, _p(topk_ids), topk, E, M,
+        _p(permute_x), _p(out_scale), _p(indice_map), _p(token_nums)))
+
+
+def prefill_permute_to_masked_gemm(x, scale, topk_ids, num_local_experts, max_token_num):
+    """The page's call: returns (permute_x [E * max_token_num, ...] with x's
+    dtype, output_scale [E, max_token_num, hidden/32] uint8, permuted_indice_map
+    [T, topk] int32, token_nums_per_expert [E, 1] int32).  Rows of permute_x
+    past an expert's count are left uninitialised."""
+    E, M = int(num_local_experts), int(max_token_num)
+    T, topk = topk_ids.shape
+    hidden = scale.shape[-1] * (512 if scale.dtype == torch.int32 else 32)
+    dev = x.device
+    px = torch.empty((E * M,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+    osf = torch.empty((E, M, hidden // 32), dtype=torch.uint8, device=dev)
+    imap = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    nums = torch.empty((E, 1), dtype=torch.int32, device=dev)
+    hq_prefill_permute_to_masked_gemm(x, scale, topk_ids, E, M, px, osf, imap, nums, hidden)
+    return px, osf, imap, nums
 
 
 # ---------------------------------------------------------------- allocation helper

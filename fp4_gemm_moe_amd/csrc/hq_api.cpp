@@ -285,4 +285,47 @@ hq_status hq_fused_swiglu_quant(void* stream, int32_t mode, const uint16_t* x, i
                   what);
 }
 
+hq_status hq_prefill_permute_to_masked_gemm(void* stream, const uint8_t* x, int64_t num_tokens,
+                                            int64_t row_bytes, int64_t hidden, const void* scale,
+                                            int32_t scale_mode, const int64_t* topk_ids,
+                                            int32_t topk, int32_t num_experts,
+                                            int64_t max_token_num, uint8_t* permute_x,
+                                            uint8_t* out_scale, int32_t* indice_map,
+                                            int32_t* token_nums) {
+  const char* what = "hq_prefill_permute_to_masked_gemm";
+  if (scale_mode != HQ_SCALE_BROADCAST && scale_mode != HQ_SCALE_DIRECT)
+    return fail(HQ_ERR_MODE, "%s: unknown scale mode %d", what, scale_mode);
+  if (num_tokens < 0) return fail(HQ_ERR_SHAPE, "%s: num_tokens=%lld < 0", what, (long long)num_tokens);
+  if (topk < 1 || topk > 64) return fail(HQ_ERR_SHAPE, "%s: topk=%d must be in [1, 64]", what, topk);
+  if (num_tokens * topk > kI32)
+    return fail(HQ_ERR_SHAPE, "%s: num_tokens * topk must be < 2^31", what);
+  if (num_experts < 1 || num_experts > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_experts=%d must be in [1, 1024]", what, num_experts);
+  if (max_token_num < 128 || max_token_num % 128 != 0 || max_token_num > kI32)
+    return fail(HQ_ERR_SHAPE, "%s: max_token_num=%lld must be a positive multiple of 128", what,
+                (long long)max_token_num);
+  if (num_experts * max_token_num > kI32)
+    return fail(HQ_ERR_SHAPE, "%s: num_experts * max_token_num must be < 2^31", what);
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(HQ_ERR_SHAPE, "%s: row_bytes=%lld must be a positive multiple of 16", what, (long long)row_bytes);
+  const int64_t hstep = scale_mode == HQ_SCALE_BROADCAST ? 512 : 128;
+  if (hidden <= 0 || hidden % hstep != 0)
+    return fail(HQ_ERR_SHAPE, "%s: hidden=%lld must be a positive multiple of %lld in this scale mode", what,
+                (long long)hidden, (long long)hstep);
+  if (!token_nums) return fail(HQ_ERR_NULL, "%s: token_nums is required", what);
+  if (num_tokens > 0 && (!x || !scale || !topk_ids || !permute_x || !out_scale || !indice_map))
+    return fail(HQ_ERR_NULL, "%s: x, scale, topk_ids, permute_x, out_scale and indice_map are required", what);
+  if (!aligned16(x) || !aligned16(permute_x))
+    return fail(HQ_ERR_ALIGN, "%s: x and permute_x must be 16-byte aligned", what);
+  if ((reinterpret_cast<uintptr_t>(scale) | reinterpret_cast<uintptr_t>(out_scale)) & 3u)
+    return fail(HQ_ERR_ALIGN, "%s: scale and out_scale must be 4-byte aligned", what);
+  hq::DeviceInfo dev;
+  hq_status st = current_device(&dev);
+  if (st != HQ_OK) return st;
+  return launched(hq::launch_permute((hipStream_t)stream, x, num_tokens, row_bytes, hidden, scale, scale_mode,
+                                     topk_ids, topk, num_experts, max_token_num, permute_x, out_scale,
+                                     indice_map, token_nums),
+                  what);
+}
+
 }  // extern "C"

@@ -194,6 +194,46 @@ hq_status hq_fused_swiglu_quant(void* stream, int32_t mode, const uint16_t* x,
                                 const int32_t* valid, uint8_t* q, uint8_t* sf,
                                 const float* global_scale, float* y_debug);
 
+/*
+ * Token permute into the masked-GEMM layout (HALOps "GEMM" page,
+ * prefill_permute_to_masked_gemm section).  For every (token t, slot j)
+ * whose expert id e = topk_ids[t, j] lies in [0, num_experts), the token's
+ * row is copied to the next free row r of expert e's slot:
+ *   permute_x[e * max_token_num + r]  = x[t]          (row_bytes bytes)
+ *   out_scale[e, r, :]                = per-32 scales of token t
+ *   indice_map[t, j]                  = r
+ * and token_nums[e] ends as the number of rows written to expert e.
+ *   x           [num_tokens, row_bytes] (FP8 codes, BF16 values or packed
+ *               FP4 codes: copied bit for bit; row_bytes % 16 == 0)
+ *   scale       HQ_SCALE_BROADCAST: int32 [num_tokens, hidden/512], byte b
+ *               (little-endian) of word w = scale of the 128-group 4w + b,
+ *               given to its four 32-groups (hidden % 512 == 0);
+ *               HQ_SCALE_DIRECT: uint8 [num_tokens, hidden/32] per-32 bytes
+ *               (hidden % 128 == 0)
+ *   topk_ids    int64 [num_tokens, topk], 1 <= topk <= 64; ids outside
+ *               [0, num_experts) (e.g. -1) are unassigned: map -1
+ *   permute_x   [num_experts * max_token_num, row_bytes]; rows past an
+ *               expert's count are not written
+ *   out_scale   uint8 [num_experts, max_token_num, hidden/32], plain
+ *               row-major (the scale layout the masked GEMM takes)
+ *   indice_map  int32 [num_tokens, topk];  token_nums  int32 [num_experts]
+ * max_token_num must be a positive multiple of 128.  Pairs beyond
+ * max_token_num for one expert are dropped (map -1; the section's kernel
+ * would write past the slot).  The order of rows inside an expert is not
+ * fixed (it follows atomic arrival); the set of rows, their contents, the
+ * counts and the map's consistency are.  x, permute_x 16-byte aligned;
+ * scale, out_scale 4-byte aligned.
+ */
+#define HQ_SCALE_BROADCAST 0
+#define HQ_SCALE_DIRECT 1
+hq_status hq_prefill_permute_to_masked_gemm(void* stream, const uint8_t* x, int64_t num_tokens,
+                                            int64_t row_bytes, int64_t hidden, const void* scale,
+                                            int32_t scale_mode, const int64_t* topk_ids,
+                                            int32_t topk, int32_t num_experts,
+                                            int64_t max_token_num, uint8_t* permute_x,
+                                            uint8_t* out_scale, int32_t* indice_map,
+                                            int32_t* token_nums);
+
 #ifdef __cplusplus
 }
 #endif

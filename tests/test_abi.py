@@ -27,10 +27,11 @@ def _declared():
     return sorted(set(re.findall(r"\b(hq_[a-z_]+)\s*\(", src)))
 
 
-def test_header_declares_the_six_calls():
+def test_header_declares_the_calls():
     names = _declared()
     for n in ["hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm", "hq_group_contiguous_gemm",
-              "hq_group_masked_gemm", "hq_fused_swiglu_quant", "hq_last_error"]:
+              "hq_group_masked_gemm", "hq_fused_swiglu_quant", "hq_prefill_permute_to_masked_gemm",
+              "hq_last_error"]:
         assert n in names
     assert set(names) == set(hq.EXPORTED_SYMBOLS)
 
@@ -135,3 +136,31 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(hq, "library_path", lambda: str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="has not been built"):
         hq.load()
+
+
+def _permute(lib, x=A, T=8, row_bytes=4096, hidden=2048, scale=A, mode=0, ids=A, topk=8, E=16, M=1024,
+             px=A, osf=A, imap=A, nums=A):
+    return lib.hq_prefill_permute_to_masked_gemm(None, x, T, row_bytes, hidden, scale, mode, ids, topk, E, M,
+                                                 px, osf, imap, nums)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=2), -4),
+    (dict(topk=0), -2),
+    (dict(topk=65), -2),
+    (dict(E=0), -2),
+    (dict(E=1025), -2),
+    (dict(M=100), -2),
+    (dict(M=0), -2),
+    (dict(row_bytes=4100), -2),
+    (dict(hidden=2176), -2),            # broadcast mode needs hidden % 512 == 0
+    (dict(mode=1, hidden=2112), -2),    # direct mode needs hidden % 128 == 0
+    (dict(T=-1), -2),
+    (dict(nums=NUL), -1),
+    (dict(x=NUL), -1),
+    (dict(x=MIS), -3),
+    (dict(osf=ctypes.c_void_p(0x10002)), -3),
+])
+def test_permute_rejects_before_launch(lib, kw, code):
+    assert _permute(lib, **kw) == code
+    assert len(lib.hq_last_error()) > 0
