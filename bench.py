@@ -14,7 +14,7 @@ of the valid rows per second), the per-kernel times, the roofline of the
 dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
 and the oracle timed on a bounded sample on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload moe|dense_fp4|masked_fp4]
+    python bench.py [--steps K] [--warmup W] [--workload moe|dense_fp4|masked_fp4|permute]
     python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
                                         # one JSON line per case
 """
@@ -201,6 +201,42 @@ def cpu_baseline_moe(ctx, budget_s=12.0):
 
 
 # ---------------------------------------------------------------- other workloads
+def run_permute(args, torch, hq, synth):
+    """Token permute into the masked layout at the shapes of the HALOps
+    "GEMM" page's prefill_permute_to_masked_gemm example (1024 tokens of
+    hidden 2048 in BF16, top-8 of 16 experts, max_token_num 1024, int32
+    broadcast scales); --tokens scales the token count."""
+    dev = torch.device("cuda:0")
+    T, H, topk, E = args.tokens, 2048, 8, 16
+    M = max(1024, ((T * topk // E) * 2 + 127) // 128 * 128)      # headroom for imbalance
+    d = synth.permute_inputs(T, H, topk, E)
+    x = _dev_bf16(torch, d["x"], dev)
+    scale = torch.from_numpy(d["scale"]).to(dev)
+    ids = torch.from_numpy(d["topk_ids"]).to(dev)
+    px = torch.empty(E * M, H, dtype=torch.bfloat16, device=dev)
+    osf = torch.empty(E, M, H // 32, dtype=torch.uint8, device=dev)
+    imap = torch.empty(T, topk, dtype=torch.int32, device=dev)
+    nums = torch.empty(E, dtype=torch.int32, device=dev)
+    f = lambda: hq.hq_prefill_permute_to_masked_gemm(x, scale, ids, E, M, px, osf, imap, nums)
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        timer.mark("permute", f)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("permute")
+    placed = int(nums.sum().item())
+    # read x, scales, ids; write the placed rows and scale rows, the map, the counts
+    bytes_ = T * (2 * H + H // 128 + 8 * topk) + placed * (2 * H + H // 32) + 4 * T * topk + 4 * E
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    cfg = {"workload": f"prefill_permute_to_masked_T{T}_H{H}_top{topk}_E{E}_M{M}_bf16_broadcast",
+           "tokens": T, "hidden": H, "topk": topk, "experts": E, "max_token_num": M}
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    return gbs, ms, cfg, roof, {"permute": {"ms": ms, "GB/s": gbs, "bytes": bytes_}}, None, "GB/s"
+
+
 def run_dense_fp4(args, torch, hq, synth):
     dev = torch.device("cuda:0")
     mode = args.mode
@@ -374,11 +410,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4", "sweep"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4", "permute", "sweep"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
     ap.add_argument("--k", type=int, default=5120)
+    ap.add_argument("--tokens", type=int, default=1024, help="--workload permute: token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (calibrates "
@@ -411,8 +448,11 @@ def main():
     if args.workload == "sweep":
         run_sweep(args, torch, hq, synth)
         return
-    runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4}[args.workload]
-    value, ms_step, cfg, roof, kernels, ctx = runner(args, torch, hq, synth)
+    runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4,
+              "permute": run_permute}[args.workload]
+    res = runner(args, torch, hq, synth)
+    value, ms_step, cfg, roof, kernels, ctx = res[:6]
+    unit = res[6] if len(res) > 6 else "TFLOP/s"
     cpu = None
     if ctx is not None and not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
@@ -420,7 +460,7 @@ def main():
     line = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -428,7 +468,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if args.workload == "moe" else args.mode,
+        "dtype": {"moe": "mxfp8", "permute": "bf16"}.get(args.workload, args.mode),
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,

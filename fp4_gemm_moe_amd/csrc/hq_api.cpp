@@ -324,7 +324,7 @@ hq_status hq_prefill_permute_to_masked_gemm(void* stream, const uint8_t* x, int6
   if (st != HQ_OK) return st;
   return launched(hq::launch_permute((hipStream_t)stream, x, num_tokens, row_bytes, hidden, scale, scale_mode,
                                      topk_ids, topk, num_experts, max_token_num, permute_x, out_scale,
-                                     indice_map, token_nums),
+                                     indice_map, token_nums, dev.num_cus),
                   what);
 }
 

@@ -65,6 +65,6 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& args, const DeviceInfo& de
 hipError_t launch_permute(hipStream_t s, const uint8_t* x, int64_t tokens, int64_t row_bytes,
                           int64_t hidden, const void* scale, int32_t scale_mode, const int64_t* ids,
                           int32_t topk, int32_t experts, int64_t max_tokens, uint8_t* out_x,
-                          uint8_t* out_scale, int32_t* map, int32_t* counts);
+                          uint8_t* out_scale, int32_t* map, int32_t* counts, int num_cus);
 
 }  // namespace hq

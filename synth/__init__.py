@@ -144,6 +144,19 @@ def moe_masked(seed=4, E=64, max_m=256, K=7168, N=4096, with_weights=True, threa
     return out
 
 
+def permute_inputs(T, H, topk, E, seed=5):
+    """Token-permute inputs shaped like the HALOps "GEMM" page's
+    prefill_permute_to_masked_gemm example: BF16 rows N(0,1) [T, H], random
+    int32 broadcast scale words [T, H/512] (bytes of UE8M0 values 120..134),
+    top-k expert ids uniform in [0, E) [T, topk] int64."""
+    rng = np.random.default_rng([seed, T, H, topk, E])
+    x = normal_bf16(rng, (T, H))
+    sb = rng.integers(120, 135, size=(T, H // 128), dtype=np.uint8)
+    scale = np.ascontiguousarray(sb).view(np.int32).reshape(T, H // 512)
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.int64)
+    return {"x": x, "scale": scale, "topk_ids": ids}
+
+
 def garbage_bytes(seed, shape):
     """Uniform random bytes (used for padded rows that must be ignored)."""
     return np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
