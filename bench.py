@@ -233,7 +233,7 @@ def run_permute(args, torch, hq, synth):
     cfg = {"workload": f"prefill_permute_to_masked_T{T}_H{H}_top{topk}_E{E}_M{M}_bf16_broadcast",
            "tokens": T, "hidden": H, "topk": topk, "experts": E, "max_token_num": M}
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+            "frac": gbs / PEAK_HBM_GBS, "traffic": _traffic("permute_bf16_T16384") if T == 16384 else None}
     return gbs, ms, cfg, roof, {"permute": {"ms": ms, "GB/s": gbs, "bytes": bytes_}}, None, "GB/s"
 
 
