@@ -14,7 +14,7 @@ of the valid rows per second), the per-kernel times, the roofline of the
 dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
 and the oracle timed on a bounded sample on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload moe|dense_fp4|masked_fp4|permute]
+    python bench.py [--steps K] [--warmup W] [--workload moe|moe_mlp|dense_fp4|masked_fp4|permute]
     python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
                                         # one JSON line per case
 """
@@ -82,7 +82,11 @@ def _traffic(kernel_key):
 
 
 # ---------------------------------------------------------------- MoE workload
-def run_moe(args, torch, hq, synth):
+def run_moe(args, torch, hq, synth, down=False):
+    """The MoE expert forward step: MXFP8 quantisation of the routed
+    activations, the grouped gate|up GEMM, the fused SwiGLU + MXFP8 re-quant;
+    with down=True also the down-projection grouped GEMM (K = H = 1536,
+    N = hidden = 4096) on the SwiGLU codes -- the whole expert MLP."""
     dev = torch.device("cuda:0")
     log("generating MoE inputs (E=32, 65536 routed rows, K=4096, N=3072)")
     d = synth.moe_contiguous(threads=16)
@@ -102,6 +106,14 @@ def run_moe(args, torch, hq, synth):
     out = torch.empty(R, N, dtype=torch.bfloat16, device=dev)
     yq = torch.empty(R, H, dtype=torch.uint8, device=dev)
     ysf = torch.empty(R, H // 32, dtype=torch.uint8, device=dev)
+    HID = 4096
+    if down:
+        log("generating down-projection weights (E=32, 4096 x 1536)")
+        w2 = _dev_bf16(torch, synth.moe_down_weights(E, HID, H, threads=16).reshape(E * HID, H), dev)
+        w2q, w2sf, _ = hq.quantize(w2, "mxfp8")
+        del w2
+        w2q, w2sf = w2q.view(E, HID, H), w2sf.view(E, HID, H // 32)
+        out2 = torch.empty(R, HID, dtype=torch.bfloat16, device=dev)
 
     timer = Timer(torch)
 
@@ -109,12 +121,17 @@ def run_moe(args, torch, hq, synth):
         f1 = lambda: hq.hq_group_wise_quant("mxfp8", x, aq, asf)
         f2 = lambda: hq.hq_group_contiguous_gemm("mxfp8", aq, asf, wq, wsf, ge, out)
         f3 = lambda: hq.hq_fused_swiglu_quant("mxfp8", out, yq, ysf, E, ge, 0, valid)
+        f4 = lambda: hq.hq_group_contiguous_gemm("mxfp8", yq, ysf, w2q, w2sf, ge, out2)
         if t is None:
             f1(); f2(); f3()
+            if down:
+                f4()
         else:
             t.mark("quant", f1)
             t.mark("gemm", f2)
             t.mark("swiglu", f3)
+            if down:
+                t.mark("down", f4)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -152,12 +169,19 @@ def run_moe(args, torch, hq, synth):
     cfg = {"workload": "moe_grouped_contiguous_mxfp8_E32_T65536_K4096_N3072_swiglu",
            "experts": E, "routed_rows": T, "padded_rows": R, "k": K, "n": N, "h": H,
            "group_align": 128}
+    if down:
+        down_ms = timer.mean_ms("down")
+        down_flops = 2.0 * T * HID * H
+        kernels["down_gemm_mxfp8"] = {"ms": down_ms, "TFLOP/s": down_flops / (down_ms * 1e-3) / 1e12,
+                                      "frac_mfma": down_flops / (down_ms * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp8"]}
+        cfg = dict(cfg, workload="moe_mlp_mxfp8_E32_T65536_K4096_H1536_hidden4096", hidden=HID)
     roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_TFLOPS["mxfp8"],
             "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_TFLOPS["mxfp8"],
             "traffic": _traffic("grouped_gemm_mxfp8"),
             "kernel": "grouped_gemm_mxfp8", "flop_per_launch": flops}
-    value = flops / (ms_step * 1e-3) / 1e12
-    ctx = {"counts": counts, "ends": ends, "a": d["a"], "b": d["b"], "K": K, "N": N, "H": H}
+    step_flops = flops + (down_flops if down else 0.0)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    ctx = None if down else {"counts": counts, "ends": ends, "a": d["a"], "b": d["b"], "K": K, "N": N, "H": H}
     return value, ms_step, cfg, roof, kernels, ctx
 
 
@@ -410,7 +434,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense_fp4", "masked_fp4", "permute", "sweep"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "moe_mlp", "dense_fp4", "masked_fp4", "permute", "sweep"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
@@ -449,7 +473,8 @@ def main():
         run_sweep(args, torch, hq, synth)
         return
     runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4,
-              "permute": run_permute}[args.workload]
+              "permute": run_permute,
+              "moe_mlp": lambda *a: run_moe(*a, down=True)}[args.workload]
     res = runner(args, torch, hq, synth)
     value, ms_step, cfg, roof, kernels, ctx = res[:6]
     unit = res[6] if len(res) > 6 else "TFLOP/s"
@@ -468,7 +493,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"moe": "mxfp8", "permute": "bf16"}.get(args.workload, args.mode),
+        "dtype": {"moe": "mxfp8", "moe_mlp": "mxfp8", "permute": "bf16"}.get(args.workload, args.mode),
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,

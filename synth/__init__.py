@@ -134,6 +134,12 @@ def moe_contiguous(seed=3, E=32, tokens=16384, topk=4, K=4096, H=1536, align=128
     return out
 
 
+def moe_down_weights(E=32, hidden=4096, H=1536, seed=3, threads=8):
+    """Down-projection weights of the MoE MLP chain [E, hidden, H] N(0, 0.02)
+    (the expert GEMM after the SwiGLU, K = H)."""
+    return normal_bf16_per_expert(seed * 1000 + 8, E, (hidden, H), 0.02, threads)
+
+
 def moe_masked(seed=4, E=64, max_m=256, K=7168, N=4096, with_weights=True, threads=8):
     rng = np.random.default_rng(seed)
     counts = moe_masked_counts(rng, E, max_m)
