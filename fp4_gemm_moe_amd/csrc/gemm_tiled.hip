@@ -453,7 +453,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   };
 
   // `mid(part, slots)` issues issue slot `part` of `slots` of the next step's
-  // loads (part -1: all of them at once; NVFP4 and inactive waves do that).
+  // loads (part -1: all of them at once, as inactive waves do).
   // pin(): keeps a step's matrix instructions ahead of the barrier that
   // follows it where branches come next (the compiler would otherwise sink
   // them past it).
@@ -509,7 +509,6 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (q + 1 < 4) load_phase(q + 1, can, cbn, san, sbn);
-        if (q == 0) mid(-1, 1);
         __builtin_amdgcn_sched_barrier(0);
         v2f fa[FI], fb[FJ];      // this lane group's two UE4M3 scales per row
 #pragma unroll
@@ -526,8 +525,12 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
           for (int i = 0; i < FI; ++i)
 #pragma unroll
-            for (int j = 0; j < FJ; ++j)
+            for (int j = 0; j < FJ; ++j) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j], da[i], acc[i][j], 0, 0, 0);
+              // the next step's loads: one slot after each MFMA of the first
+              // sub-step (3 % faster than all at once ahead of it)
+              if (q == 0 && u == 0) mid(i * FJ + j, FI * FJ);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (q + 1 < 4) {
