@@ -721,24 +721,24 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
           for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
             const int bl = 2 * e, bh = 2 * e + 1;
-            // group 0 receives the partner's b = 2e quad, group 1 the partner's
-            // b = 2e+1 quad: V_PERMLANE32_SWAP(x = quad 2e, y = quad 2e+1)
-            // leaves x = {x[0..31], y[0..31]} and y = {x[32..63], y[32..63]},
-            // so group 0 takes y and group 1 takes x
-            // (NVFP4 keeps the LDS-routed lane exchange: with the swap its
-            // kernel runs out of registers)
-            uint32_t r0, r1;
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            v4u o;
             if constexpr (FMT != kNV) {
+              // V_PERMLANE32_SWAP(x = quad 2e, y = quad 2e+1) leaves
+              // x = {x[0..31], y[0..31]} and y = {x[32..63], y[32..63]}: in
+              // either lane group (x, y) are then the first and second four
+              // columns of the lane's 8-column run
               const auto sw0 = __builtin_amdgcn_permlane32_swap(pk[bl][0], pk[bh][0], false, false);
               const auto sw1 = __builtin_amdgcn_permlane32_swap(pk[bl][1], pk[bh][1], false, false);
-              r0 = h == 0 ? sw0[1] : sw0[0];
-              r1 = h == 0 ? sw1[1] : sw1[0];
+              o = v4u{sw0[0], sw1[0], sw0[1], sw1[1]};
             } else {
-              r0 = (uint32_t)__shfl_xor((int)(h == 0 ? pk[bh][0] : pk[bl][0]), 32, 64);
-              r1 = (uint32_t)__shfl_xor((int)(h == 0 ? pk[bh][1] : pk[bl][1]), 32, 64);
+              // (NVFP4 keeps the LDS-routed exchange: with the swap its kernel
+              // runs out of registers)  group 0 receives the partner's b = 2e
+              // quad, group 1 the partner's b = 2e+1 quad
+              const uint32_t r0 = (uint32_t)__shfl_xor((int)(h == 0 ? pk[bh][0] : pk[bl][0]), 32, 64);
+              const uint32_t r1 = (uint32_t)__shfl_xor((int)(h == 0 ? pk[bh][1] : pk[bl][1]), 32, 64);
+              o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
             }
-            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-            v4u o = h == 0 ? v4u{pk[bl][0], pk[bl][1], r0, r1} : v4u{r0, r1, pk[bh][0], pk[bh][1]};
             const int64_t n = tl.n0 + wn * WTN + j * 32 + 8 * (h == 0 ? bl : bh);
             const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, (int)off, 0, 0);
