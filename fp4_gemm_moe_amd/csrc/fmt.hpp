@@ -45,11 +45,6 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
   return e < 0 ? 0u : (uint32_t)e;
 }
 
-// 2^-(byte - 127) as an FP32 (exact, normal for every byte in [0, 246]).
-__device__ __forceinline__ float mx_inv_scale(uint32_t byte) {
-  return __uint_as_float((254u - byte) << 23);
-}
-
 // |v| (FP32) -> E4M3 magnitude code with round-to-nearest-even, saturating
 // at 448 (code 0x7E).  Normal results keep 3 of FP32's 23 mantissa bits (add
 // 0x7FFFF plus the kept LSB, truncate); results below 2^-6 sit on the fixed
