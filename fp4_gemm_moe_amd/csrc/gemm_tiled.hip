@@ -374,7 +374,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   int total_gm, n_heavy = 0;
   if (p.form == kUniform) total_gm = G0 * mt_per;
   else total_gm = build_tiled_table<FMT>(p, tt, n_heavy);
-  const int total = total_gm * NT * (p.ksplit > 1 ? p.ksplit : 1);
+  int total = total_gm * NT * (p.ksplit > 1 ? p.ksplit : 1);
+  if (p.tile_limit > 0 && p.tile_limit < total) total = p.tile_limit;   // a leading run of tiles
 
   const int tid = threadIdx.x;
   const int w = ufirst(tid >> 6);                           // wave index (uniform)
@@ -768,6 +769,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   const int64_t plane = p.m_rows * p.n;          // floats per slice
   const int64_t chunks = p.n / 4;
+  const int64_t ldo = p.ldo > 0 ? p.ldo : p.n;
   for (int64_t row = blockIdx.x; row < p.m_rows; row += gridDim.x) {
     const int64_t g = row / p.slot_rows;
     const float alpha = p.mode == kNVFP4 ? p.alpha[g] : 1.0f;
@@ -790,7 +792,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) f[r] = v[r];
       }
-      *reinterpret_cast<uint2*>(p.out + e) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      *reinterpret_cast<uint2*>(p.out + row * ldo + 4 * c) =
+          make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
     }
   }
 }
@@ -846,6 +849,74 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   const int64_t tiles = gm_upper * NT;
   int cus = dev.num_cus;
   if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+
+  // Tail split (dense form): when the tiles fill some rounds of the grid and
+  // leave a last round at most half full, that round's tiles -- the last
+  // ones in the tile order, a rectangle of whole n-tile columns of the last
+  // block of 4 m-tiles -- run as a second, K-split launch on the rectangle,
+  // so they occupy the CUs with S times smaller units.  It pays only when a
+  // tile is long next to writing and summing its S partial planes: at least
+  // about 110 us of matrix work per tail tile on a loaded chip, i.e. 40 FP4
+  // steps, 48 FP8 steps or 12 NVFP4 steps (whose BF16 products are slower).
+  constexpr int64_t kTailMinSteps = FMT == kNV ? 12 : (FMT == 0 ? 48 : 40);
+  const int64_t grid_full = cus >= 8 ? cus - cus % 8 : cus;
+  const int64_t nk_all = p.lda / SROW;
+  if (p.form == kUniform && p.num_groups == 1 && tiles > grid_full && nk_all >= kTailMinSteps &&
+      p.n * 1024 < ((int64_t)1 << 31)) {
+    const int64_t tail = tiles % grid_full;
+    const int64_t total_gm = (p.m_rows + BM - 1) / BM;
+    const int64_t last_blk = (total_gm - 1) / 4;
+    const int64_t mb = total_gm - last_blk * 4;           // m-tiles of the last block
+    const int64_t cols = (tail + mb - 1) / mb;            // n-tile columns of the rectangle
+    int64_t S = cols * mb > 0 ? grid_full / (cols * mb) : 0;
+    if (S > nk_all / 4) S = nk_all / 4;
+    if (S > 8) S = 8;
+    if (tail > 0 && tail * 2 <= grid_full && cols < NT && S >= 2) {
+      const int64_t r0 = last_blk * 4 * BM, c0 = (NT - cols) * BN;
+      GemmArgs q2 = p;
+      q2.a = p.a + r0 * p.lda;
+      q2.sfa = p.sfa + r0 * p.ldsf;
+      q2.b = p.b + c0 * p.lda;
+      q2.sfb = p.sfb + c0 * p.ldsf;
+      q2.out = p.out + r0 * p.n + c0;
+      q2.bias = p.bias ? p.bias + c0 : nullptr;
+      q2.m_rows = p.m_rows - r0;
+      q2.slot_rows = q2.m_rows;
+      q2.n = p.n - c0;
+      q2.ldo = p.n;
+      q2.ksplit = (int32_t)S;
+      q2.tile_limit = 0;
+      hipMemPool_t pool = workspace_pool(dev.device);
+      void* ws = nullptr;
+      if (pool != nullptr &&
+          hipMallocFromPoolAsync(&ws, (size_t)(S * q2.m_rows * q2.n * 4), pool, s) == hipSuccess) {
+        q2.partial = static_cast<float*>(ws);
+        GemmArgs q1 = p;
+        q1.ksplit = 1;
+        q1.partial = nullptr;
+        q1.tile_limit = (int32_t)(tiles - cols * mb);
+        hipLaunchKernelGGL((mx_gemm_tiled<FMT, false>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
+                           s, q1);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess) {
+          int64_t g2 = cols * mb * S;
+          if (g2 > grid_full) g2 = grid_full;
+          if (g2 >= 8) g2 -= g2 % 8;
+          hipLaunchKernelGGL((mx_gemm_tiled<FMT, true>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
+          e = hipGetLastError();
+        }
+        if (e == hipSuccess) {
+          int64_t rgrid = (int64_t)cus * 4;
+          if (q2.m_rows < rgrid) rgrid = q2.m_rows;
+          hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q2);
+          e = hipGetLastError();
+        }
+        const hipError_t ef = hipFreeAsync(ws, s);
+        return e != hipSuccess ? e : ef;
+      }
+      (void)hipGetLastError();        // no workspace: run unsplit
+    }
+  }
 
   // K split where the tiles cannot fill half of the CUs (dense and batch
   // forms): S slices of at least 4 K steps each, S * tiles <= CUs, at most 8.

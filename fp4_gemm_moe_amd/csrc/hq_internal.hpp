@@ -46,6 +46,8 @@ struct GemmArgs {
   // in order and writes the BF16 output.  Set by the tiled launcher.
   int32_t ksplit;
   float* partial;
+  int64_t ldo;          // output row stride in elements (0: n); the K-split reduce only
+  int32_t tile_limit;   // tiled kernel: process only the first tile_limit tiles (0: all)
 };
 
 struct DeviceInfo {

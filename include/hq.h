@@ -15,7 +15,8 @@
  *    device).  The caller allocates and owns every buffer; the library keeps
  *    no pointer after a call returns and never synchronises the host.  The
  *    one allocation it makes is the FP32 workspace of a K-split dense or
- *    batch GEMM (see hq_dense_gemm), taken from and returned to the
+ *    batch GEMM or of a dense GEMM's K-split last round (see hq_dense_gemm),
+ *    taken from and returned to the
  *    library's own per-device stream-ordered pool inside the call's stream
  *    order.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and is stream-ordered, so a call may be captured into a graph.
@@ -114,6 +115,11 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x,
  * workspace comes from the library's stream-ordered pool; if it cannot be
  * had, the call runs unsplit.  FP32 summation order (not the result's
  * contract) then differs from an unsplit call.
+ * When the tiles fill whole rounds of the compute units and leave a last
+ * round at most half full, and K is long (at least 48 MXFP8, 40 MXFP4 or 12
+ * NVFP4 steps), the last round's tiles -- whole 256-column tiles of the last
+ * 1024 rows or fewer -- are computed the same way, K-split into a workspace
+ * of slices * rows * columns floats of that rectangle, after the other tiles.
  */
 hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
                         const uint8_t* sfa, const uint8_t* b,

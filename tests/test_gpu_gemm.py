@@ -26,13 +26,21 @@ pytestmark = pytest.mark.gpu
 SENTINEL = 0x7FC1   # a BF16 NaN pattern no kernel produces
 
 
+def _code_lut(table):
+    lut = np.zeros(int(max(table)) + 1, np.uint8)
+    for v, c in table.items():
+        lut[int(v)] = c
+    return lut
+
+
 def _int_operand(rng, rows, k, mode, choices):
     vals = rng.choice(np.array(choices), (rows, k))
+    mag = np.abs(vals)
     if mode == "mxfp8":
-        codes = np.vectorize(lambda v: INT_E4M3[abs(v)] | (0x80 if v < 0 else 0))(vals).astype(np.uint8)
+        codes = _code_lut(INT_E4M3)[mag] | np.where(vals < 0, 0x80, 0).astype(np.uint8)
         sf = np.full((rows, k // 32), 127, np.uint8)
     else:
-        c = np.vectorize(lambda v: INT_E2M1[abs(v)] | (0x8 if v < 0 else 0))(vals).astype(np.uint8)
+        c = _code_lut(INT_E2M1)[mag] | np.where(vals < 0, 0x8, 0).astype(np.uint8)
         codes = F.pack_nibbles(c)
         sf = np.full((rows, k // (16 if mode == "nvfp4" else 32)), 0x38 if mode == "nvfp4" else 127, np.uint8)
     return vals, codes, sf
@@ -46,11 +54,12 @@ def _quant(bits, mode):
     return c, s, None
 
 
-def _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None):
+def _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None, cu_limit=0):
     out = torch.full((m, n), 0, dtype=torch.int16, device=dev).view(torch.bfloat16)
     hq.hq_dense_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
                      out, bias=None if bias is None else U.dev_bf16(bias, dev),
-                     alpha=None if alpha is None else torch.tensor([alpha], dtype=torch.float32, device=dev))
+                     alpha=None if alpha is None else torch.tensor([alpha], dtype=torch.float32, device=dev),
+                     cu_limit=cu_limit)
     torch.cuda.synchronize()
     return U.host_bits(out)
 
@@ -138,6 +147,48 @@ def test_k_split_random(mode):
     got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha)
     want = G.dense_gemm(mode, a, sfa, b, sfb, bias, alpha)
     U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"k-split {mode}")
+
+
+# A dense launch whose last round of tiles is at most half full: the leading
+# tiles run unsplit and the last ones -- whole n-tile columns of the last
+# block of 4 m-tiles -- run K-split as a sub-problem whose reduce writes into
+# the full-width output.  It is taken for long K only (48 FP8, 40 FP4 or 12
+# NVFP4 steps and more).  A CU limit sets the round size at these sizes:
+#   520 x 1544 (3 x 7 tiles, 16 CUs): 5 tail tiles -> 2 columns x 3 m-tiles,
+#     the rectangle spans every row, 2 slices; 1100 x 1544 (5 x 7 tiles, 32
+#     CUs): 3 tail tiles -> 3 columns of the ragged fifth m-tile (rows
+#     1024..1099), 8 uneven slices of 49 or 41 K steps.
+TAIL_SPLIT_CASES = [("mxfp8", 520, 1544, 6144, 16), ("mxfp8", 1100, 1544, 6272, 32),
+                    ("mxfp4", 1100, 1544, 10496, 32), ("nvfp4", 520, 1544, 3072, 16)]
+
+
+@pytest.mark.parametrize("case", TAIL_SPLIT_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-cu{c[4]}")
+def test_tail_split_integer_exact(case):
+    mode, m, n, k, cus = case
+    dev = U.require_gpu()
+    U.banner(f"tail split int-exact {mode} m={m} n={n} k={k} cu_limit={cus}")
+    rng = np.random.default_rng(m + n + k)
+    av, a, sfa = _int_operand(rng, m, k, mode, [-1, 0, 1])
+    bv, b, sfb = _int_operand(rng, n, k, mode, [-1, 0, 1])
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None, cu_limit=cus)
+    want = F.bf16_round(av.astype(np.float64) @ bv.astype(np.float64).T)   # exact: |sums| <= k
+    assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("case", TAIL_SPLIT_CASES[1:2] + TAIL_SPLIT_CASES[3:],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-cu{c[4]}")
+def test_tail_split_random_with_bias_or_alpha(case):
+    mode, m, n, k, cus = case
+    dev = U.require_gpu()
+    U.banner(f"tail split random {mode} m={m} n={n} k={k} cu_limit={cus}")
+    rng = np.random.default_rng(3 * m + k)
+    a, sfa, ga = _quant(synth.normal_bf16(rng, (m, k)), mode)
+    b, sfb, gb = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
+    alpha = None if ga is None else np.float32(ga * gb)
+    bias = synth.normal_bf16(rng, (n,), 0.1) if mode == "mxfp8" else None
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha, cu_limit=cus)
+    want = G.dense_gemm(mode, a, sfa, b, sfb, bias, alpha)
+    U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"tail split {mode}")
 
 
 def test_k_split_batch_with_bias():
