@@ -129,21 +129,15 @@ __global__ void nv_gs_finalize(float* gs) {
 }
 
 // NVFP4: per 16-group (two lanes of 8), sf = UE4M3(amax_b / (6 g)),
-// s_eff = decode(sf) * g, code = E2M1(x / s_eff); IEEE FP32 divisions.
+// s_eff = decode(sf) * g, code = E2M1(x / s_eff) with correctly rounded FP32
+// quotients.
 __device__ __forceinline__ void nv_emit(const Chunk8& c, uint32_t amax_bits, float g, float d,
                                         int64_t ci, uint8_t* __restrict__ q,
                                         uint8_t* __restrict__ sf) {
   float ratio = __uint_as_float(amax_bits) / d;
   uint32_t sb = e4m3_mag(__float_as_uint(ratio) & 0x7fffffffu);
   float s_eff = e4m3_value(sb) * g;
-  uint32_t w = 0;
-  if (s_eff != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_code(c.f[i] / s_eff) << (4 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(c.f[i]) >> 28) & 8u) << (4 * i);
-  }
+  const uint32_t w = nv_fp4x8(c.f, s_eff);
   reinterpret_cast<uint32_t*>(q)[ci] = w;
   if ((ci & 1) == 0) sf[ci >> 1] = (uint8_t)sb;
 }

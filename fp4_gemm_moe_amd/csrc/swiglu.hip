@@ -44,14 +44,7 @@ __device__ __forceinline__ void emit(const Y8& y, int64_t row, int64_t chunk, in
     float ratio = __uint_as_float(m) / d;
     uint32_t sb = e4m3_mag(__float_as_uint(ratio) & 0x7fffffffu);
     float s_eff = e4m3_value(sb) * g;
-    uint32_t w = 0;
-    if (s_eff != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= e2m1_code(y.f[i] / s_eff) << (4 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(y.f[i]) >> 28) & 8u) << (4 * i);
-    }
+    const uint32_t w = nv_fp4x8(y.f, s_eff);
     reinterpret_cast<uint32_t*>(q + row * (h / 2))[chunk] = w;
     if ((chunk & 1) == 0) sf[row * (h / 16) + (chunk >> 1)] = (uint8_t)sb;
     return;

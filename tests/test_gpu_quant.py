@@ -86,6 +86,26 @@ def test_quant_every_bf16_value(mode):
     _check(mode, np.ascontiguousarray(out), dev, what="all finite BF16")
 
 
+@pytest.mark.parametrize("g", [2.0 ** -100, 2.0 ** -40, 0.0012345, 1.0, 2.0 ** 40, 2.0 ** 100])
+def test_quant_nvfp4_every_bf16_value(g):
+    """Every normal BF16 pattern of either sign, sorted by magnitude into
+    16-groups (so each group's scale is set by values of one size, and every
+    value meets an unsaturated scale at some global scale), groups and group
+    members shuffled.  The global scales put the effective block scales both
+    inside [2^-56, 2^56], where the device divides with a shared reciprocal,
+    and outside it, where it divides plainly."""
+    dev = U.require_gpu()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ex = bits & 0x7F80
+    vals = bits[(ex != 0x7F80) & (ex != 0)]
+    vals = vals[np.argsort(vals & 0x7FFF, kind="stable")]
+    vals = vals[: (len(vals) // 16) * 16].reshape(-1, 16)
+    rng = np.random.default_rng(int(np.log2(g)) + 200)
+    vals = rng.permuted(vals, axis=1)[rng.permutation(len(vals))]
+    out = np.ascontiguousarray(vals.reshape(-1, 256)[: (vals.size // 256)])
+    _check("nvfp4", out, dev, g=g, what=f"all normal BF16, g={g:g}")
+
+
 def test_quant_nvfp4_supplied_global_scale():
     dev = U.require_gpu()
     rng = np.random.default_rng(3)
