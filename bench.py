@@ -29,7 +29,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4_bf16": 2500.0}
+PEAK_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4_f16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8/MXFP4 grouped GEMM TFLOP/s + % MFMA peak; quant/SwiGLU GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -283,7 +283,7 @@ def run_dense_fp4(args, torch, hq, synth):
     ms = timer.mean_ms("gemm")
     flops = 2.0 * m * n * k
     tf = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["nvfp4_bf16" if mode == "nvfp4" else mode]
+    peak = PEAK_TFLOPS["nvfp4_f16" if mode == "nvfp4" else mode]
     gs = 16 if mode == "nvfp4" else 32
     bytes_ = (m + n) * k * (0.5 + 1 / gs) + 2 * m * n
     cfg = {"workload": f"dense_{mode}_M{m}_N{n}_K{k}", "m": m, "n": n, "k": k}
@@ -385,7 +385,7 @@ def run_sweep(args, torch, hq, synth):
                 flops = 2.0 * m * n * k
                 gs = 16 if mode == "nvfp4" else 32
                 bytes_ = (m + n) * k * (0.5 + 1 / gs) + 2 * m * n
-                peak = PEAK_TFLOPS["nvfp4_bf16" if mode == "nvfp4" else mode]
+                peak = PEAK_TFLOPS["nvfp4_f16" if mode == "nvfp4" else mode]
                 t_ideal = max(flops / (peak * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e6
                 t = cold if cold is not None else warm
                 emit({"case": "dense_gemm", "mode": mode, "m": m, "n": n, "k": k,

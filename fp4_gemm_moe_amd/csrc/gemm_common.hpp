@@ -34,7 +34,8 @@ namespace hq {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // FMT: 0 = FP8 E4M3 operands, 4 = FP4 E2M1 operands (the instruction's
 // cbsz / blgp format codes).
@@ -43,25 +44,17 @@ __device__ __forceinline__ v4f mfma_scaled(v8i w, v8i x, v4f acc, int sw, int sx
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, FMT, FMT, 0, sw, 0, sx);
 }
 
-// 8 nibbles times one UE4M3 scale -> 8 BF16 (exact: the product has at most
-// 6 significant bits and lies in [2^-10, 2688]).  Nibbles decode to FP32 with
-// the hardware FP4 conversion (scale 1), two per instruction; the products
-// are packed to BF16 two per instruction.
-__device__ __forceinline__ v8bf decode8(uint32_t w, float sc) {
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  const v2f f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
-                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
-  v8bf r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const v2bf h = __builtin_convertvector((v2f{f[b][0] * sc, f[b][1] * sc}), v2bf);
-    r[2 * b] = h[0];
-    r[2 * b + 1] = h[1];
-  }
-  return r;
+// 8 nibbles times one UE4M3 scale -> 8 FP16 (exact: a product has at most
+// 6 significant bits and lies in [2^-10, 2688], inside FP16's normal range).
+// Nibbles decode to FP16 with the hardware FP4 conversion (scale 1) and take
+// the scale with packed FP16 multiplies, two values per instruction each.
+__device__ __forceinline__ v8h decode8(uint32_t w, _Float16 sc) {
+  const h2 s2 = {sc, sc};
+  const h2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const h2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const h2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const h2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return v8h{f0[0], f0[1], f1[0], f1[1], f2[0], f2[1], f3[0], f3[1]};
 }
 
 // Rows owned by group g and the tile space (group m-tiles x n-tiles).

@@ -9,10 +9,10 @@
 //   * any K with k % 32 == 0 (a lane's K slice is exactly one 32-group, so a
 //     ragged K tail is a per-lane predicate: zero codes, unit scale);
 //   * NVFP4 in those shapes (UE4M3 scales per 16 cannot be folded into the
-//     E8M0-scaled instruction, so codes are decoded to BF16 -- exactly: an
-//     E2M1 value times a UE4M3 value has at most 6 significant bits -- and
-//     multiplied on the BF16 matrix cores; alpha = g_A * g_B is applied in
-//     FP32).
+//     E8M0-scaled instruction, so codes are decoded to FP16 -- exactly: an
+//     E2M1 value times a UE4M3 value has at most 6 significant bits and lies
+//     in FP16's normal range -- and multiplied on the FP16 matrix cores;
+//     alpha = g_A * g_B is applied in FP32).
 #include <mutex>
 #include <vector>
 
@@ -239,12 +239,12 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
 
 // ---------------------------------------------------------------- NVFP4
 // Lane slice for NVFP4: 32 elements [32 kb, 32 kb + 32) of a row (16 bytes)
-// and the two UE4M3 scales of its 16-groups.  The four BF16 MFMAs of one K
+// and the two UE4M3 scales of its 16-groups.  The four FP16 MFMAs of one K
 // step consume its elements 8s..8s+7 (s = 0..3); the same K permutation is
 // applied to both operands, so the dot products are unchanged.
 struct NvSlice {
   uint4 codes;
-  float s0, s1;
+  _Float16 s0, s1;       // the two UE4M3 scales (exact in FP16)
 };
 
 __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8_t* row_sf, int kb,
@@ -252,11 +252,11 @@ __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8
   NvSlice s;
   if (kin) {
     s.codes = *reinterpret_cast<const uint4*>(row_codes + (int64_t)kb * 16);
-    s.s0 = e4m3_value(row_sf[(int64_t)kb * 2] & 0x7Fu);
-    s.s1 = e4m3_value(row_sf[(int64_t)kb * 2 + 1] & 0x7Fu);
+    s.s0 = (_Float16)e4m3_value(row_sf[(int64_t)kb * 2] & 0x7Fu);
+    s.s1 = (_Float16)e4m3_value(row_sf[(int64_t)kb * 2 + 1] & 0x7Fu);
   } else {
     s.codes = make_uint4(0, 0, 0, 0);
-    s.s0 = s.s1 = 0.0f;
+    s.s0 = s.s1 = (_Float16)0.0f;
   }
   return s;
 }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
             out2[e].codes = in ? *reinterpret_cast<const uint4*>(rc + (int64_t)kb * 16) : make_uint4(0, 0, 0, 0);
             // bytes 8e + 2q and 8e + 2q + 1 of the pair: dword 2e + q/2, half q & 1
             const uint32_t d = e == 0 ? (q < 2 ? s16.x : s16.y) : (q < 2 ? s16.z : s16.w);
-            const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((d >> (16 * (q & 1))) & 0x7F7Fu, 1.0f, false);
+            const h2 f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((d >> (16 * (q & 1))) & 0x7F7Fu, 1.0f, false);
             out2[e].s0 = f[0];
             out2[e].s1 = f[1];
           }
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          v8bf ad[FM], bd[FN];
+          v8h ad[FM], bd[FN];
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
             const uint4 c = as[u][fm].codes;
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
           for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bd[fn], ad[fm], acc[fm][fn], 0, 0, 0);
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bd[fn], ad[fm], acc[fm][fn], 0, 0, 0);
         }
       }
     }

@@ -1,5 +1,5 @@
 // LDS-tiled, double-buffered GEMM for the MX modes (MXFP8 and MXFP4, scaled
-// MFMA) and NVFP4 (exact BF16 decode, BF16 MFMA) -- the large-M tier of the flashrt/fp4-gemm page's M-tiered dispatch
+// MFMA) and NVFP4 (exact FP16 decode, FP16 MFMA) -- the large-M tier of the flashrt/fp4-gemm page's M-tiered dispatch
 // and the grouped MoE GEMMs of the HALOps "GEMM" page (group_contiguous_gemm,
 // group_masked_gemm, batch_gemm sections).
 //
@@ -476,9 +476,9 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       return;
     }
     if constexpr (FMT == kNV) {
-      // NVFP4: codes decode exactly to BF16 (E2M1 value x UE4M3 scale, at
-      // most 6 significant bits) and multiply on the BF16 matrix cores,
-      // V_MFMA_F32_32X32X16_BF16.  A stage is 4 phases of 64 K; in phase q a
+      // NVFP4: codes decode exactly to FP16 (E2M1 value x UE4M3 scale, at
+      // most 6 significant bits, normal FP16 range) and multiply on the FP16
+      // matrix cores, V_MFMA_F32_32X32X16_F16 (the BF16 rate).  A stage is 4 phases of 64 K; in phase q a
       // lane reads 16-byte chunk 2q + h of each fragment row (32 codes) and
       // scale dword q of the row (the 4 UE4M3 bytes of the phase's 16-groups;
       // this lane group's are bytes 2h and 2h + 1).  Sub-step u of the phase
@@ -511,14 +511,17 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       for (int q = 0; q < 4; ++q) {
         if (q + 1 < 4) load_phase(q + 1, can, cbn, san, sbn);
         __builtin_amdgcn_sched_barrier(0);
-        v2f fa[FI], fb[FJ];      // this lane group's two UE4M3 scales per row
+        // this lane group's two UE4M3 scales per row (bit 7 ignored: unsigned)
+        h2 fa[FI], fb[FJ];
 #pragma unroll
-        for (int i = 0; i < FI; ++i) fa[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa[i] >> (16 * h), 1.0f, false);
+        for (int i = 0; i < FI; ++i)
+          fa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((sa[i] >> (16 * h)) & 0x7F7Fu, 1.0f, false);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) fb[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[j] >> (16 * h), 1.0f, false);
+        for (int j = 0; j < FJ; ++j)
+          fb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((sb[j] >> (16 * h)) & 0x7F7Fu, 1.0f, false);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          v8bf da[FI], db[FJ];
+          v8h da[FI], db[FJ];
 #pragma unroll
           for (int i = 0; i < FI; ++i) da[i] = decode8(word(ca[i], u), fa[i][u >> 1]);
 #pragma unroll
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
           for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j], da[i], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(db[j], da[i], acc[i][j], 0, 0, 0);
               // the next step's loads: one slot after each MFMA of the first
               // sub-step (3 % faster than all at once ahead of it)
               if (q == 0 && u == 0) mid(i * FJ + j, FI * FJ);

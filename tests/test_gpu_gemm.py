@@ -116,6 +116,23 @@ def test_dense_random_small(mode):
         U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"{mode} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("mnk", [(5, 520, 512), (300, 264, 512)], ids=["direct", "tiled"])
+def test_nvfp4_scale_sign_bit_ignored(mnk):
+    """UE4M3 scales are unsigned: a scale byte with bit 7 set decodes as the
+    byte without it, in both the skinny and the tiled kernels."""
+    dev = U.require_gpu()
+    m, n, k = mnk
+    U.banner(f"nvfp4 scale bit 7 m={m} n={n} k={k}")
+    rng = np.random.default_rng(m + 17)
+    a = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    b = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    sfa = (rng.integers(0x20, 0x48, (m, k // 16)) | (rng.integers(0, 2, (m, k // 16)) << 7)).astype(np.uint8)
+    sfb = (rng.integers(0x20, 0x48, (n, k // 16)) | (rng.integers(0, 2, (n, k // 16)) << 7)).astype(np.uint8)
+    got = _dense_gpu("nvfp4", a, sfa, b, sfb, m, n, k, dev, alpha=1.0)
+    want = G.dense_gemm("nvfp4", a, sfa, b, sfb, alpha=np.float32(1.0))
+    U.assert_gemm_close(got, want, U.deq("nvfp4", a, sfa), U.deq("nvfp4", b, sfb), np.float32(1.0), "scale bit 7")
+
+
 # Few tiles and a long K: the tiled kernel splits K into slices (uneven here)
 # whose FP32 partial tiles a second kernel sums before the BF16 rounding.
 K_SPLIT_SHAPES = {"mxfp8": (300, 520, 8576), "mxfp4": (200, 264, 8448), "nvfp4": (130, 512, 8448)}
