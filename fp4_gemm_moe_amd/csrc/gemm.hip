@@ -1,7 +1,8 @@
 // GEMM dispatch by mode, form and shape (the M-tiered dispatch of the
 // flashrt/fp4-gemm page, re-chosen for gfx950):
 //   * more than 16 rows per group and K a multiple of the K step (128 for
-//     MXFP8, 256 for MXFP4 and NVFP4): the LDS-tiled persistent kernel;
+//     MXFP8, 256 for MXFP4 and NVFP4) of at least two steps: the LDS-tiled
+//     persistent kernel;
 //   * skinny M (<= 16 rows per group) and any other K: the direct kernel.
 #include "gemm_common.hpp"
 

@@ -33,10 +33,11 @@
 //     that the 32 consecutive tiles one XCD (one L2) runs side by side cover
 //     4 row tiles x 8 column tiles.
 // Requirements (checked by the dispatcher): K % 128 == 0 (FP8) or
-// K % 256 == 0 (FP4); scale pointers 4-byte aligned; lda * 256 < 2^31;
+// K % 256 == 0 (FP4), at least two K steps; scale pointers 4-byte aligned; lda * 256 < 2^31;
 // n * 512 < 2^31.
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "gemm_common.hpp"
 
@@ -382,9 +383,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   const int lane = tid & 63;
   const int wm = w / WGN, wn = w % WGN;                     // wave grid (M x N)
   const int h = lane >> 5, r32 = lane & 31;
-  const int nk = (int)(p.lda / SROW);          // K steps of a whole row
-  // more than one K step in every tile (K-split ranges have at least two)
-  const bool multi = p.ksplit > 1 || nk > 1;
+  const int nk = (int)(p.lda / SROW);          // K steps of a whole row (at least 2)
 
   // XCD-aware order: workgroup b runs on XCD b % 8; inside a round of
   // gridDim tiles XCD x owns a contiguous run of tiles.  Rounds alternate
@@ -470,7 +469,12 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // runs the epilogue, whose stores then fall outside the tile's bounds.
   bool active = true;
   constexpr int kLoadRows = 4;
-  auto step = [&](const uint8_t* cur, auto&& mid) {
+  // A tile's step 0 (kFirst) starts its accumulators from zero: its first
+  // sub-step's matrix instructions take a zero accumulator operand, so the
+  // accumulators are never cleared separately.  (A wave that skips its matrix
+  // work keeps the previous tile's values; its stores are all out of bounds.)
+  auto step = [&](const uint8_t* cur, auto&& mid, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     if (!active) {
       mid(-1, 1);
       return;
@@ -530,7 +534,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
           for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(db[j], da[i], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  db[j], da[i], kFirst && q == 0 && u == 0 ? v16f{} : acc[i][j], 0, 0, 0);
               // the next step's loads: one slot after each MFMA of the first
               // sub-step (3 % faster than all at once ahead of it)
               if (q == 0 && u == 0) mid(i * FJ + j, FI * FJ);
@@ -581,7 +586,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
         const v8i af = op(fa);
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-          acc[i][j] = mfma32<FMT>(op(fb[j]), af, acc[i][j], sc(bsc[j], v), sc(asc[i], v));
+          acc[i][j] = mfma32<FMT>(op(fb[j]), af, kFirst && v == 0 ? v16f{} : acc[i][j], sc(bsc[j], v),
+                                  sc(asc[i], v));
           // the next step's loads ride between the MFMAs of the first kLoadRows
           // rows, one issue slot after each (measured: 3 % faster than issuing
           // them all ahead of one row; the wave that stalls on a full address
@@ -603,43 +609,39 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
   issue<FMT>(tl, lo, 0, smem_lds, w);
-  if (multi) {
-    issue<FMT>(tl, lo, 1, smem_lds + C::STAGE, w);
-    wait_vm<C::OPS>();
-  } else {
-    wait_vm<0>();
-  }
+  issue<FMT>(tl, lo, 1, smem_lds + C::STAGE, w);
+  wait_vm<C::OPS>();
   bar();
+
+  // cleared once, so that a wave without matrix work in its first tile
+  // stores defined values (out of bounds, dropped)
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   bool prior_stores = false;
   while (true) {
     active = wm * WTM < tl.row_end - tl.row0;
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Steps 0 .. nk-2.  Step 1's loads were issued with step 0's, before the
     // previous tile's stores; step k >= 1 issues step k + 1 into the stage
     // step k - 1 used.
-    auto nothing = [](int, int) {};
-    if (multi) {
-      // step 0: step 1's loads were issued with step 0's, before the previous
-      // tile's stores, which stay in flight
-      step(smem + st * C::STAGE, nothing);
-      pin();
-      __builtin_amdgcn_sched_barrier(0);
-      if (prior_stores) wait_vm<kStores>();
-      else wait_vm<0>();
-      bar();
-      st ^= 1;
-    }
+    // step 0: step 1's loads were issued with step 0's, before the previous
+    // tile's stores, which stay in flight
+    step(smem + st * C::STAGE, [](int, int) {}, std::true_type{});
+    pin();
+    __builtin_amdgcn_sched_barrier(0);
+    if (prior_stores) wait_vm<kStores>();
+    else wait_vm<0>();
+    bar();
+    st ^= 1;
     for (int k = 1; k + 1 < tl.nk; ++k) {
       const uint32_t nxt = smem_lds + (st ^ 1) * C::STAGE;
       step(smem + st * C::STAGE,
-           [&](int part, int slots) { issue<FMT>(tl, lo, k + 1, nxt, w, part, slots); });
+           [&](int part, int slots) { issue<FMT>(tl, lo, k + 1, nxt, w, part, slots); }, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<0>();
       bar();
@@ -653,10 +655,10 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next);
       issue<FMT>(tn, lo, 0, smem_lds + (st ^ 1) * C::STAGE, w);
     }
-    step(smem + st * C::STAGE, [](int, int) {});
+    step(smem + st * C::STAGE, [](int, int) {}, std::false_type{});
     pin();
     bar();                            // stage `st` is free
-    if (has_next && multi) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
+    if (has_next) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
 
     if constexpr (SPLIT) {
       // ---- K-split epilogue: this slice's FP32 partial tile to
@@ -753,8 +755,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     if (!has_next) break;
     // the next tile's step 0 was issued before its step 1 (nk > 1) and these
     // kStores stores
-    if (multi) wait_vm<C::OPS + kStores>();
-    else wait_vm<kStores>();
+    wait_vm<C::OPS + kStores>();
     bar();
     t = t_next;
     ++round;
@@ -967,7 +968,7 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
 
 bool tiled_supported(const GemmArgs& p) {
   const int64_t step = p.mode == kMXFP8 ? 128 : 256;
-  if (p.k % step != 0) return false;
+  if (p.k % step != 0 || p.k < 2 * step) return false;   // at least two K steps
   if ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 3) return false;
   if (p.lda * 256 >= (int64_t)1 << 31) return false;
   if (p.n * 256 * 2 > 0x7FFFFFFFLL) return false;   // 32-bit output offsets below the drop marker

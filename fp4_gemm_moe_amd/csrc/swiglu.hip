@@ -143,7 +143,7 @@ hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64
                                int64_t slot_rows, const int32_t* valid, uint8_t* q,
                                uint8_t* sf, const float* gs, float* y_debug) {
   int64_t blocks = (rows + 3) / 4;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 8192) blocks = 8192;     // 32 per CU (measured 5 % faster than 16)
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks), block(kThreads);
 #define HQ_SWIGLU(M)                                                                      \
