@@ -128,7 +128,32 @@ struct Cfg {
   // vector-memory ops per stage per thread: each wave loads the scale
   // dwords of 512 / WAVES rows (of A or B with 8 waves, of both with 4)
   static constexpr int SOPS = (BM + BN) / (WAVES * 64);
-  static constexpr int OPS = 2 * LOADS + SOPS * PLANES;
+};
+
+// LDS layout and scale-load schedule.  GS (grouped scales): a row's scale
+// bytes are fetched 16 at a time -- SPG consecutive K steps' worth (4 FP8,
+// 2 FP4, 1 NVFP4 steps) -- by one 16-byte load per row into one of two
+// scale buffers [BM + BN rows][16 bytes] next to the two operand stages.
+// Each such load touches one cache line per row, so against one dword load
+// per row and 4-byte plane per step this cuts the memory transactions of
+// the scales 4x (the scale loads touched as many cache lines as the operand
+// loads; without them the MX GEMMs ran 13-21 % faster).  It needs a row's
+// scale bytes to be a multiple of 16 (K % 512 == 0 for MX); otherwise each
+// stage carries its step's scales as dword planes (plane h of row r at
+// h * rows + r), one dword load per row and plane.
+template <int FMT, bool GS>
+struct Lay {
+  using C = Cfg<FMT>;
+  static constexpr int STAGE = C::A_BYTES + C::B_BYTES + (GS ? 0 : (BM + BN) * C::SB);
+  static constexpr int SBUF = (BM + BN) * 16;          // one scale buffer (GS)
+  static constexpr int SMEM = 2 * STAGE + (GS ? 2 * SBUF : 0);
+  static constexpr int SPG = GS ? 16 / C::SB : 1;      // K steps per scale load
+  static constexpr int RS = GS ? 16 : 4;               // LDS bytes from row to row
+  static constexpr int PS = GS ? 4 : BM * 4;           // LDS bytes from plane to plane
+  static constexpr int BOFF = BM * (GS ? 16 : C::SB);  // B's scales after A's
+  // vector-memory operations of a step that loads scales, and of step 1
+  static constexpr int SCALE_OPS = GS ? C::SOPS : C::SOPS * C::PLANES;
+  static constexpr int OPS1 = 2 * C::LOADS + (SPG == 1 ? SCALE_OPS : 0);
 };
 
 // Grouped forms: per group its end row and the inclusive prefixes of its
@@ -195,14 +220,17 @@ __device__ int build_tiled_table(const GemmArgs& p, TiledTable& t, int& n_heavy)
 struct Tile {
   int g;
   int nk, slice;                 // K steps of this tile (range), K-split slice
+  int sg;                        // scale buffer of the tile's first scale group (GS)
   int64_t row0, row_end, n0;
   const uint8_t *a, *b, *sa, *sb;
   int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
 };
 
+// `unit`: K-split slice boundaries fall on multiples of this many steps (a
+// scale group with grouped scales).
 template <int FMT>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& tt, int total_gm,
-                                          int n_heavy, int NT, int mt_per, int nk, int t) {
+                                          int n_heavy, int NT, int mt_per, int nk, int t, int unit) {
   // K split: units are numbered slice-major, so that neighbouring units of
   // one slice share operand rows as without a split
   const int S = p.ksplit > 1 ? p.ksplit : 1;
@@ -242,9 +270,11 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
     row_end = row0 + BM < ge ? row0 + BM : ge;
   }
   Tile tl;
+  tl.sg = 0;
   tl.g = (int)ufirst((uint32_t)g);
-  // this slice's K steps [k0, k1) of the nk steps
-  const int k0 = (int)((int64_t)slice * nk / S), k1 = (int)((int64_t)(slice + 1) * nk / S);
+  // this slice's K steps [k0, k1) of the nk steps, on multiples of `unit`
+  const int ng = nk / unit;
+  const int k0 = unit * (int)((int64_t)slice * ng / S), k1 = unit * (int)((int64_t)(slice + 1) * ng / S);
   tl.slice = (int)ufirst((uint32_t)slice);
   tl.nk = (int)ufirst((uint32_t)(k1 - k0));
   const int64_t kb = (int64_t)ufirst((uint32_t)k0) * SROW, ksb = (int64_t)ufirst((uint32_t)k0) * Cfg<FMT>::SB;
@@ -291,31 +321,57 @@ __device__ __forceinline__ LoadOffsets<FMT> make_offsets(const GemmArgs& p, int 
   return o;
 }
 
-// Issues K step k of tile `tl` into the LDS stage at byte address `base`:
-// Cfg<FMT>::OPS operations.  With part >= 0 only the operations of one of
-// `slots` issue slots are issued (the 2 LOADS tile loads spread evenly over
-// the slots, the scale loads with the last tile load); calls for every slot
-// 0 .. slots-1 together issue the whole step in the same order.
-template <int FMT>
+// Issues K step k of tile `tl` into the LDS stage at byte address `base`
+// (lds0: the LDS byte address of the dynamic LDS): 2 LOADS operand loads and
+// the step's scale loads, if it has any.  part -1 issues all of them.  With
+// part >= 0 only the operand loads of one of `slots` issue slots are issued
+// (the 2 LOADS loads spread evenly over the slots; per-step scale planes ride
+// with the last one); calls for every slot 0 .. slots-1 together issue the
+// operand loads in the same order.  part -2 issues only grouped scale loads:
+// the step calls it ahead of its matrix instructions, because the branch on
+// the step's place in its scale group would otherwise let the compiler sink
+// the instructions before it below it and bunch up the operand loads.
+template <int FMT, bool GS>
 __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o, int k, uint32_t base,
-                                      int w, int part = -1, int slots = 1) {
+                                      uint32_t lds0, int w, int part = -1, int slots = 1) {
   using C = Cfg<FMT>;
+  using L = Lay<FMT, GS>;
   constexpr int LOADS = C::LOADS, WAVES = C::WAVES;
   const uint32_t la = base + w * 1024;
   const uint32_t lb = la + C::A_BYTES;
   const int64_t ka = (int64_t)k * SROW, ks = (int64_t)k * C::SB;
   const __amdgpu_buffer_rsrc_t ra = rsrc(tl.a + ka, tl.a_bytes - ka);
   const __amdgpu_buffer_rsrc_t rb = rsrc(tl.b + ka, tl.b_bytes - ka);
+  if (part != -2) {
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    if (part < 0 || part == i * slots / (2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
+    for (int i = 0; i < LOADS; ++i)
+      if (part < 0 || part == i * slots / (2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    if (part < 0 || part == (LOADS + i) * slots / (2 * LOADS)) dma16(rb, o.tile[i], lb + i * WAVES * 1024);
-  if (part >= 0 && part != (2 * LOADS - 1) * slots / (2 * LOADS)) return;
-  // scale planes: dword plane h of row r at plane h * rows + r.  With four
-  // waves wave w loads rows [64 w, 64 w + 64) of A and of B; with eight,
-  // waves 0-3 those rows of A and waves 4-7 of B.
+    for (int i = 0; i < LOADS; ++i)
+      if (part < 0 || part == (LOADS + i) * slots / (2 * LOADS)) dma16(rb, o.tile[i], lb + i * WAVES * 1024);
+  }
+  // Scales.  With four waves wave w loads rows [64 w, 64 w + 64) of A and of
+  // B; with eight, waves 0-3 those rows of A and waves 4-7 of B.
+  if constexpr (GS) {
+    // the first step of a scale group: the group's 16 bytes of every row
+    // into scale buffer (sg + group) % 2, row r at 16 r
+    if (part >= 0 || k % L::SPG != 0) return;
+    const uint32_t sbuf = lds0 + 2 * L::STAGE + ((tl.sg + k / L::SPG) & 1) * L::SBUF;
+    const uint32_t lsa = sbuf + ((w * 64) % BM) * 16;
+    const uint32_t lsb = lsa + L::BOFF;
+    const __amdgpu_buffer_rsrc_t rsa = rsrc(tl.sa + ks, tl.sa_bytes - ks);
+    const __amdgpu_buffer_rsrc_t rsb = rsrc(tl.sb + ks, tl.sb_bytes - ks);
+    if constexpr (C::SOPS == 2) {
+      dma16(rsa, o.scale, lsa);
+      dma16(rsb, o.scale, lsb);
+    } else {
+      const bool is_a = w * 64 < BM;
+      dma16(is_a ? rsa : rsb, o.scale, is_a ? lsa : lsb);
+    }
+    return;
+  }
+  if (part == -2 || (part >= 0 && part != (2 * LOADS - 1) * slots / (2 * LOADS))) return;
+  // dword plane h of row r at plane h * rows + r
   const uint32_t lsa = base + C::A_BYTES + C::B_BYTES + ((w * 64) % BM) * 4;
   const uint32_t lsb = lsa + BM * C::SB;
   const __amdgpu_buffer_rsrc_t rsa = rsrc(tl.sa + ks, tl.sa_bytes - ks);
@@ -361,9 +417,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // SPLIT: the launch has a K split (p.ksplit > 1) and the epilogue writes
 // FP32 partial tiles instead of the BF16 output (a separate instantiation, so
 // that the second epilogue costs the single-pass kernel no registers).
-template <int FMT, bool SPLIT>
+template <int FMT, bool SPLIT, bool GS>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
+  using L = Lay<FMT, GS>;
   constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
   constexpr int kStores = C::kStores;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -453,7 +510,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   };
 
   // `mid(part, slots)` issues issue slot `part` of `slots` of the next step's
-  // loads (part -1: all of them at once, as inactive waves do).
+  // loads (part -1: all of them at once, as inactive waves do; part -2: its
+  // grouped scale loads).
   // pin(): keeps a step's matrix instructions ahead of the barrier that
   // follows it where branches come next (the compiler would otherwise sink
   // them past it).
@@ -473,7 +531,9 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // sub-step's matrix instructions take a zero accumulator operand, so the
   // accumulators are never cleared separately.  (A wave that skips its matrix
   // work keeps the previous tile's values; its stores are all out of bounds.)
-  auto step = [&](const uint8_t* cur, auto&& mid, auto first) {
+  // `scl`: the step's scale words (row r of A at scl + r * RS, plane q at
+  // + q * PS; B's rows from scl + BOFF).
+  auto step = [&](const uint8_t* cur, const uint8_t* scl, auto&& mid, auto first) {
     constexpr bool kFirst = decltype(first)::value;
     if (!active) {
       mid(-1, 1);
@@ -490,8 +550,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       // both operands use this same K order, so the products pair up.
       const uint8_t* la = cur + wm * WTM * SROW;
       const uint8_t* lb = cur + C::A_BYTES + wn * WTN * SROW;
-      const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WTM + r32) * 4;
-      const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WTN + r32) * 4;
+      const uint8_t* lsa = scl + (wm * WTM + r32) * L::RS;
+      const uint8_t* lsb = scl + L::BOFF + (wn * WTN + r32) * L::RS;
       typedef float v2f __attribute__((ext_vector_type(2)));
       uint4 ca[FI], cb[FJ], can[FI], cbn[FJ];
       uint32_t sa[FI], sb[FJ], san[FI], sbn[FJ];
@@ -499,18 +559,19 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
           xa[i] = rd16(la, i, 2 * q);
-          ya[i] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
+          ya[i] = lds_read4(lsa + q * L::PS + 32 * i * L::RS);
         }
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
           xb[j] = rd16(lb, j, 2 * q);
-          yb[j] = lds_read4(lsb + q * BN * 4 + 32 * j * 4);
+          yb[j] = lds_read4(lsb + q * L::PS + 32 * j * L::RS);
         }
       };
       auto word = [](const uint4& c, int u) -> uint32_t {
         return u == 0 ? c.x : (u == 1 ? c.y : (u == 2 ? c.z : c.w));
       };
       load_phase(0, ca, cb, sa, sb);
+      mid(-2, 1);                     // the next step's scales, ahead of the matrix work
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (q + 1 < 4) load_phase(q + 1, can, cbn, san, sbn);
@@ -559,8 +620,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
     const uint8_t* la = cur + wm * WTM * SROW;
     const uint8_t* lb = cur + C::A_BYTES + wn * WTN * SROW;
-    const uint8_t* lsa = cur + C::A_BYTES + C::B_BYTES + (wm * WTM + r32) * 4;
-    const uint8_t* lsb = cur + C::A_BYTES + C::B_BYTES + BM * C::SB + (wn * WTN + r32) * 4;
+    const uint8_t* lsa = scl + (wm * WTM + r32) * L::RS;
+    const uint8_t* lsb = scl + L::BOFF + (wn * WTN + r32) * L::RS;
     Frag fa = rd(la, 0, 0);
     Frag fb[FJ], fbn[FJ];
     fb[0] = rd(lb, 0, 0);
@@ -568,12 +629,13 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
     for (int q = 0; q < C::PLANES; ++q) {
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) bsc[j][q] = lds_read4(lsb + q * BN * 4 + 32 * j * 4);
+      for (int j = 0; j < FJ; ++j) bsc[j][q] = lds_read4(lsb + q * L::PS + 32 * j * L::RS);
 #pragma unroll
-      for (int i = 0; i < FI; ++i) asc[i][q] = lds_read4(lsa + q * BM * 4 + 32 * i * 4);
+      for (int i = 0; i < FI; ++i) asc[i][q] = lds_read4(lsa + q * L::PS + 32 * i * L::RS);
     }
 #pragma unroll
     for (int j = 1; j < FJ; ++j) fb[j] = rd(lb, j, 0);
+    if constexpr (GS) mid(-2, 1);     // the next step's scales, ahead of the matrix work
 #pragma unroll
     for (int v = 0; v < SUB; ++v) {
 #pragma unroll
@@ -604,14 +666,21 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
   };
 
-  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t);
+  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t, L::SPG);
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
-  issue<FMT>(tl, lo, 0, smem_lds, w);
-  issue<FMT>(tl, lo, 1, smem_lds + C::STAGE, w);
-  wait_vm<C::OPS>();
+  issue<FMT, GS>(tl, lo, 0, smem_lds, smem_lds, w);
+  issue<FMT, GS>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
+  wait_vm<L::OPS1>();
   bar();
+  // the scale words of step k of tile `tl` in stage `stage`
+  auto scl = [&](const Tile& tt_, int k, int stage) -> const uint8_t* {
+    if constexpr (GS)
+      return smem + 2 * L::STAGE + ((tt_.sg + k / L::SPG) & 1) * L::SBUF + (k % L::SPG) * C::PLANES * 4;
+    else
+      return smem + stage * L::STAGE + C::A_BYTES + C::B_BYTES;
+  };
 
   // cleared once, so that a wave without matrix work in its first tile
   // stores defined values (out of bounds, dropped)
@@ -631,7 +700,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     // step k - 1 used.
     // step 0: step 1's loads were issued with step 0's, before the previous
     // tile's stores, which stay in flight
-    step(smem + st * C::STAGE, [](int, int) {}, std::true_type{});
+    step(smem + st * L::STAGE, scl(tl, 0, st), [](int, int) {}, std::true_type{});
     pin();
     __builtin_amdgcn_sched_barrier(0);
     if (prior_stores) wait_vm<kStores>();
@@ -639,9 +708,10 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     bar();
     st ^= 1;
     for (int k = 1; k + 1 < tl.nk; ++k) {
-      const uint32_t nxt = smem_lds + (st ^ 1) * C::STAGE;
-      step(smem + st * C::STAGE,
-           [&](int part, int slots) { issue<FMT>(tl, lo, k + 1, nxt, w, part, slots); }, std::false_type{});
+      const uint32_t nxt = smem_lds + (st ^ 1) * L::STAGE;
+      step(smem + st * L::STAGE, scl(tl, k, st),
+           [&](int part, int slots) { issue<FMT, GS>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
+           std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<0>();
       bar();
@@ -652,13 +722,15 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     const bool has_next = t_next < total;
     Tile tn = tl;
     if (has_next) {
-      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next);
-      issue<FMT>(tn, lo, 0, smem_lds + (st ^ 1) * C::STAGE, w);
+      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG);
+      // the scale buffer after this tile's last scale group
+      tn.sg = (tl.sg + tl.nk / L::SPG) & 1;
+      issue<FMT, GS>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
     }
-    step(smem + st * C::STAGE, [](int, int) {}, std::false_type{});
+    step(smem + st * L::STAGE, scl(tl, tl.nk - 1, st), [](int, int) {}, std::false_type{});
     pin();
     bar();                            // stage `st` is free
-    if (has_next) issue<FMT>(tn, lo, 1, smem_lds + st * C::STAGE, w);
+    if (has_next) issue<FMT, GS>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
 
     if constexpr (SPLIT) {
       // ---- K-split epilogue: this slice's FP32 partial tile to
@@ -755,7 +827,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     if (!has_next) break;
     // the next tile's step 0 was issued before its step 1 (nk > 1) and these
     // kStores stores
-    wait_vm<C::OPS + kStores>();
+    wait_vm<L::OPS1 + kStores>();
     bar();
     t = t_next;
     ++round;
@@ -829,19 +901,18 @@ hipMemPool_t workspace_pool(int device) {
   return pools[device];
 }
 
-template <int FMT>
+template <int FMT, bool GS>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
-  using C = Cfg<FMT>;
-  const int smem = 2 * C::STAGE;
+  const int smem = Lay<FMT, GS>::SMEM;
   // the dynamic-LDS attribute, once per device and instantiation (setting it
   // twice from racing threads is harmless)
   static std::atomic<bool> attr_set[64];
   const bool cached = dev.device >= 0 && dev.device < 64;
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, false>,
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, false, GS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, true, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               smem);
     if (e != hipSuccess) return e;
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
@@ -899,14 +970,14 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
         q1.ksplit = 1;
         q1.partial = nullptr;
         q1.tile_limit = (int32_t)(tiles - cols * mb);
-        hipLaunchKernelGGL((mx_gemm_tiled<FMT, false>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
+        hipLaunchKernelGGL((mx_gemm_tiled<FMT, false, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
                            s, q1);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess) {
           int64_t g2 = cols * mb * S;
           if (g2 > grid_full) g2 = grid_full;
           if (g2 >= 8) g2 -= g2 % 8;
-          hipLaunchKernelGGL((mx_gemm_tiled<FMT, true>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
+          hipLaunchKernelGGL((mx_gemm_tiled<FMT, true, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
           e = hipGetLastError();
         }
         if (e == hipSuccess) {
@@ -947,9 +1018,9 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
   if (q.ksplit > 1)
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, true>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, true, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   else
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, false>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, false, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   hipError_t e = hipGetLastError();
   if (q.ksplit > 1) {
     if (e == hipSuccess) {
@@ -976,9 +1047,12 @@ bool tiled_supported(const GemmArgs& p) {
 }
 
 hipError_t launch_gemm_tiled(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
-  if (p.mode == kMXFP8) return launch_tiled_cfg<0>(s, p, dev);
-  if (p.mode == kNVFP4) return launch_tiled_cfg<kNV>(s, p, dev);
-  return launch_tiled_cfg<4>(s, p, dev);
+  // grouped scale loads where a row's scale bytes are a multiple of 16 (NVFP4:
+  // always, K % 256 == 0 gives K / 16 % 16 == 0)
+  const bool gs = p.ldsf % 16 == 0;
+  if (p.mode == kNVFP4) return launch_tiled_cfg<kNV, true>(s, p, dev);
+  if (p.mode == kMXFP8) return gs ? launch_tiled_cfg<0, true>(s, p, dev) : launch_tiled_cfg<0, false>(s, p, dev);
+  return gs ? launch_tiled_cfg<4, true>(s, p, dev) : launch_tiled_cfg<4, false>(s, p, dev);
 }
 
 }  // namespace hq
