@@ -135,13 +135,19 @@ def test_nvfp4_scale_sign_bit_ignored(mnk):
 
 # Few tiles and a long K: the tiled kernel splits K into slices (uneven here)
 # whose FP32 partial tiles a second kernel sums before the BF16 rounding.
-K_SPLIT_SHAPES = {"mxfp8": (300, 520, 8576), "mxfp4": (200, 264, 8448), "nvfp4": (130, 512, 8448)}
+# K % 512 == 0 (MX) makes a row's scale bytes a multiple of 16, so the kernel
+# loads each row's scales 16 bytes (several K steps) at a time and the slices
+# start on those groups (17 groups over 8 slices here); other K take the
+# per-step scale planes.
+K_SPLIT_SHAPES = [("mxfp8", 300, 520, 8576), ("mxfp4", 200, 264, 8448), ("nvfp4", 130, 512, 8448),
+                  ("mxfp8", 300, 520, 8704), ("mxfp4", 200, 264, 8704)]
+_KS_IDS = [f"{c[0]}-k{c[3]}" for c in K_SPLIT_SHAPES]
 
 
-@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
-def test_k_split_integer_exact(mode):
+@pytest.mark.parametrize("case", K_SPLIT_SHAPES, ids=_KS_IDS)
+def test_k_split_integer_exact(case):
     dev = U.require_gpu()
-    m, n, k = K_SPLIT_SHAPES[mode]
+    mode, m, n, k = case
     U.banner(f"k-split int-exact {mode} m={m} n={n} k={k}")
     rng = np.random.default_rng(k + m)
     av, a, sfa = _int_operand(rng, m, k, mode, [-1, 0, 1])
@@ -151,10 +157,10 @@ def test_k_split_integer_exact(mode):
     assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
 
 
-@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
-def test_k_split_random(mode):
+@pytest.mark.parametrize("case", K_SPLIT_SHAPES, ids=_KS_IDS)
+def test_k_split_random(case):
     dev = U.require_gpu()
-    m, n, k = K_SPLIT_SHAPES[mode]
+    mode, m, n, k = case
     U.banner(f"k-split random {mode} m={m} n={n} k={k}")
     rng = np.random.default_rng(7 * k + n)
     a, sfa, ga = _quant(synth.normal_bf16(rng, (m, k)), mode)
