@@ -97,11 +97,28 @@ __device__ __forceinline__ v8i load_codes(const uint8_t* row_codes, int t, int q
 // grouped forms, whose tile table takes 256 threads) split K: wave w takes K
 // steps w, w + NW, ..., U steps per trip so that U loads per operand are in
 // flight per wave; the NW partial tiles are summed through LDS.
-// SC8 (K % 256 == 0, scale rows 8-byte aligned): the K steps go to the waves
-// in pairs (pair j = steps 2j, 2j + 1, wave w takes pairs w, w + NW, ...) and
-// a lane reads the 8 scale bytes of a pair in one load (its lane group's
-// bytes are q and 4 + q) instead of one byte per step.
-template <int FMT, int FM, int FN, int NWMAX, int U, bool SC8 = false>
+// SP > 1 (K % (128 SP) == 0, scale rows 4 SP-byte aligned): the K steps go to
+// the waves in groups of SP (group j = steps SP j .. SP j + SP - 1, wave w
+// takes groups w, w + NW, ...) and a lane reads the 4 SP scale bytes of a
+// group in one 8- or 16-byte load (its lane group's bytes are q, 4 + q, ...)
+// instead of one byte per step: one memory transaction per row for SP steps.
+template <int SP>
+__device__ __forceinline__ void scale_words(const uint8_t* p, bool in, uint32_t (&w)[SP]) {
+  if constexpr (SP == 2) {
+    const uint2 v = in ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+    static_assert(SP == 4, "groups of 2 or 4 K steps");
+    const uint4 v = in ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  }
+}
+
+template <int FMT, int FM, int FN, int NWMAX, int U, int SP = 1>
 __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
@@ -153,32 +170,34 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (SC8) {
-      static_assert(U % 2 == 0, "whole pairs per trip");
-      const int npairs = ksteps >> 1;
-      for (int p0 = w; p0 < npairs; p0 += NW * (U / 2)) {
+    if constexpr (SP > 1) {
+      static_assert(U % SP == 0, "whole scale groups per trip");
+      const int ngroups = ksteps / SP;
+      for (int p0 = w; p0 < ngroups; p0 += NW * (U / SP)) {
         v8i af[U][FM], bf[U][FN];
         int sa[U][FM], sb[U][FN];
 #pragma unroll
-        for (int v = 0; v < U / 2; ++v) {
+        for (int v = 0; v < U / SP; ++v) {
           const int pp = p0 + NW * v;
-          const bool in = pp < npairs;
+          const bool in = pp < ngroups;
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
-            const uint2 s8 = in ? *reinterpret_cast<const uint2*>(asf[fm] + 8 * (int64_t)pp) : make_uint2(0u, 0u);
+            uint32_t sw[SP];
+            scale_words<SP>(asf[fm] + 4 * SP * (int64_t)pp, in, sw);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              af[2 * v + e][fm] = load_codes<FMT>(arow[fm], 2 * pp + e, q, in);
-              sa[2 * v + e][fm] = (int)(((e == 0 ? s8.x : s8.y) >> (8 * q)) & 0xFFu);
+            for (int e = 0; e < SP; ++e) {
+              af[SP * v + e][fm] = load_codes<FMT>(arow[fm], SP * pp + e, q, in);
+              sa[SP * v + e][fm] = (int)((sw[e] >> (8 * q)) & 0xFFu);
             }
           }
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            const uint2 s8 = in ? *reinterpret_cast<const uint2*>(bsf[fn] + 8 * (int64_t)pp) : make_uint2(0u, 0u);
+            uint32_t sw[SP];
+            scale_words<SP>(bsf[fn] + 4 * SP * (int64_t)pp, in, sw);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              bf[2 * v + e][fn] = load_codes<FMT>(brow[fn], 2 * pp + e, q, in);
-              sb[2 * v + e][fn] = (int)(((e == 0 ? s8.x : s8.y) >> (8 * q)) & 0xFFu);
+            for (int e = 0; e < SP; ++e) {
+              bf[SP * v + e][fn] = load_codes<FMT>(brow[fn], SP * pp + e, q, in);
+              sb[SP * v + e][fn] = (int)((sw[e] >> (8 * q)) & 0xFFu);
             }
           }
         }
@@ -448,11 +467,11 @@ int64_t tile_count(const GemmArgs& p, int TM, int TN) {
 // has a resident block at once (a second, partial round of blocks would
 // nearly double the time).  Grouped forms need at least 4 waves.
 template <class K>
-int skinny_waves(K kernel, int nwmax, const GemmArgs& p, int TM, int TN, const DeviceInfo& dev) {
+int skinny_waves(K kernel, int nwmax, const GemmArgs& p, int TM, int TN, const DeviceInfo& dev, int sp = 1) {
   const int64_t tiles = tile_count(p, TM, TN);
   int cus = dev.num_cus;
   if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
-  const int64_t ksteps = (p.k / 32 + 3) / 4;
+  const int64_t ksteps = (p.k / 32 + 3) / 4 / sp;      // units of work dealt to the waves
   const int lo = p.form == kUniform ? 1 : 4;
   int hi = nwmax;
   if (ksteps < hi) hi = ksteps > lo ? (int)ksteps : lo;
@@ -500,13 +519,18 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
     if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
     return launch_direct(s, nv_gemm_direct<4, 2, 4, 1>, p, 64, 32, dev);
   }
-  // scale rows in whole, 8-byte aligned pairs of K steps
-  const bool sc8 = p.k % 256 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 7) == 0;
+  // scale rows in whole, aligned groups of 2 or 4 K steps (8 or 16 bytes)
+  const uintptr_t sfal = reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb);
+  const bool sc8 = p.k % 256 == 0 && (sfal & 7) == 0;
+  const bool sc16 = p.k % 512 == 0 && (sfal & 15) == 0;
   if (p.mode == kMXFP8) {
     if (fm == 1) {
+      if (sc16) {
+        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 4>;
+        return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev, 4));
+      }
       if (sc8) {
-        auto k = mx_gemm_direct<0, 1, 1, 16, 4, true>;
+        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 2>;
         return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
       }
       auto k = mx_gemm_direct<0, 1, 1, 16, 4>;
@@ -516,8 +540,12 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
     return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2>, p, 64, 64, dev);
   }
   if (fm == 1) {
+    if (sc16) {
+      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 4>;
+      return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev, 4));
+    }
     if (sc8) {
-      auto k = mx_gemm_direct<4, 1, 1, 16, 4, true>;
+      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 2>;
       return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
     }
     auto k = mx_gemm_direct<4, 1, 1, 16, 4>;
