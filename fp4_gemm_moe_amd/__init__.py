@@ -19,6 +19,7 @@ __all__ = [
     "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
+    "hq_group_contiguous_gemm_swiglu_quant",
     "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
     "HQ_SCALE_BROADCAST", "HQ_SCALE_DIRECT",
     "hq_last_error", "library_path", "load", "EXPORTED_SYMBOLS",
@@ -38,7 +39,7 @@ MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
 EXPORTED_SYMBOLS = (
     "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
-    "hq_prefill_permute_to_masked_gemm",
+    "hq_group_contiguous_gemm_swiglu_quant", "hq_prefill_permute_to_masked_gemm",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,8 @@ _SIGS = {
     "hq_batch_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                   _I64, _I64, _I64, _I32], _I32),
+    "hq_group_contiguous_gemm_swiglu_quant": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP,
+                                               _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_group_masked_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _VP, _VP, _VP,
                               _I64, _I64, _I32], _I32),
     "hq_fused_swiglu_quant": ([_VP, _I32, _VP, _I64, _I64, _I32, _VP, _I64, _VP, _VP, _VP,
@@ -199,6 +202,31 @@ def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, al
     _check(load().hq_group_contiguous_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
                                            _p(group_end), E, _p(bias), _p(alpha), _p(out),
                                            rows, n, k, cu_limit))
+
+
+def hq_group_contiguous_gemm_swiglu_quant(mode, a, sfa, b, sfb, group_end, q, sf, valid=None,
+                                          bias=None, y_debug=None, cu_limit=0):
+    """The gate|up grouped-contiguous GEMM (b [E, 2h, k]) with SwiGLU and the
+    MXFP8 re-quant in its epilogue: q [rows, h], sf [rows, h/32] as
+    hq_fused_swiglu_quant would write them from the GEMM's BF16 output."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    E, n, _ = b.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    h = n // 2
+    _need(a, "a", torch.uint8, rows * code_cols(mode, k))
+    _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
+    _need(b, "b", torch.uint8, E * n * code_cols(mode, k))
+    _need(sfb, "sfb", torch.uint8, E * n * (k // group_size(mode)))
+    _need(group_end, "group_end", torch.int32, E)
+    _need(valid, "valid", torch.int32, E)
+    _need(bias, "bias", torch.bfloat16, E * n)
+    _need(q, "q", torch.uint8, rows * h)
+    _need(sf, "sf", torch.uint8, rows * (h // 32))
+    _need(y_debug, "y_debug", torch.float32, rows * h)
+    _check(load().hq_group_contiguous_gemm_swiglu_quant(
+        _stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(group_end), E, _p(valid), _p(bias),
+        _p(q), _p(sf), _p(y_debug), rows, h, k, cu_limit))
 
 
 def hq_group_masked_gemm(mode, a, sfa, b, sfb, masked_m, out, max_m, bias=None, alpha=None,

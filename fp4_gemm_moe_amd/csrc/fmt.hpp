@@ -180,6 +180,16 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// SwiGLU of one element, y = up * gate * sigmoid(gate) in FP32 (HALOps "GEMM"
+// page, fused_swiglu_quant section): exp(-gate) through the hardware exp2,
+// 1/(1+e) through the hardware reciprocal.  Large negative gates give
+// e = +Inf and y = 0.  Shared by the SwiGLU kernel and the GEMM's SwiGLU
+// epilogue, so both produce the same y bits from the same BF16 gate/up.
+__device__ __forceinline__ float silu_mul(float gate, float up) {
+  float e = __builtin_amdgcn_exp2f(-gate * 1.4426950408889634f);
+  return up * gate * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Max over the 4 lanes of a DPP quad (lanes 4j..4j+3), on non-negative FP32
 // bit patterns (integer order == float order).
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {

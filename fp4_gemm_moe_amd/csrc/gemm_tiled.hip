@@ -222,15 +222,19 @@ struct Tile {
   int nk, slice;                 // K steps of this tile (range), K-split slice
   int sg;                        // scale buffer of the tile's first scale group (GS)
   int64_t row0, row_end, n0;
+  int64_t vend;                  // end of the rows an epilogue writes (SwiGLU: the valid rows)
   const uint8_t *a, *b, *sa, *sb;
   int64_t a_bytes, b_bytes, sa_bytes, sb_bytes;
 };
 
 // `unit`: K-split slice boundaries fall on multiples of this many steps (a
 // scale group with grouped scales).
+// tile_cols: output columns per n-tile (BN; 128 y columns for the SwiGLU epilogue,
+// whose tile spans 128 gate and 128 up weight rows).
 template <int FMT>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& tt, int total_gm,
-                                          int n_heavy, int NT, int mt_per, int nk, int t, int unit) {
+                                          int n_heavy, int NT, int mt_per, int nk, int t, int unit,
+                                          int tile_cols) {
   // K split: units are numbered slice-major, so that neighbouring units of
   // one slice share operand rows as without a split
   const int S = p.ksplit > 1 ? p.ksplit : 1;
@@ -280,7 +284,14 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
   const int64_t kb = (int64_t)ufirst((uint32_t)k0) * SROW, ksb = (int64_t)ufirst((uint32_t)k0) * Cfg<FMT>::SB;
   tl.row0 = ufirst64(row0);
   tl.row_end = ufirst64(row_end);
-  tl.n0 = (int64_t)nt * BN;
+  tl.vend = tl.row_end;
+  if (p.valid != nullptr) {         // the first valid[g] rows of the group (contiguous form)
+    const int64_t gs = ufirst64(group_start(p, tt, tl.g));
+    int64_t c = p.valid[tl.g];
+    c = c < 0 ? 0 : c;
+    if (gs + c < tl.vend) tl.vend = ufirst64(gs + c);
+  }
+  tl.n0 = (int64_t)nt * tile_cols;
   const int64_t brow0 = (int64_t)tl.g * p.n + tl.n0;          // first weight row
   const int64_t brows = (int64_t)p.num_groups * p.n;
   tl.a = uniform_ptr(p.a + tl.row0 * p.lda + kb);
@@ -301,23 +312,36 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
 // fills LDS rows [(i*4 + w) * 8, +8) of the A and of the B tile; lane j ->
 // row + j/8, physical chunk j % 8, logical chunk (j % 8) ^ swz(row).  Scale
 // dwords: wave w loads rows [64w, 64w + 64).
-template <int FMT>
+// PAIRED (the gate|up GEMM with the SwiGLU epilogue): B-tile row r holds the
+// weight row paired_row(r) past the tile's first gate row, so that fragment
+// j < 2 of a wave holds gate columns and fragment j + 2 the up columns of the
+// same 32 outputs: r = 128 wn + 32 j + t -> y column 64 wn + 32 (j & 1) + t,
+// plus h for the up half (j >= 2).
+__device__ __forceinline__ int paired_row(int r, int64_t h) {
+  return 64 * (r >> 7) + 32 * ((r >> 5) & 1) + (r & 31) + ((r >> 6) & 1) * (int)h;
+}
+
+template <int FMT, bool PAIRED>
 struct LoadOffsets {
   uint32_t tile[Cfg<FMT>::LOADS];
-  uint32_t scale;
+  uint32_t btile[PAIRED ? Cfg<FMT>::LOADS : 1];   // B's own offsets (PAIRED)
+  uint32_t scale, bscale;
 };
 
-template <int FMT>
-__device__ __forceinline__ LoadOffsets<FMT> make_offsets(const GemmArgs& p, int w, int lane) {
+template <int FMT, bool PAIRED>
+__device__ __forceinline__ LoadOffsets<FMT, PAIRED> make_offsets(const GemmArgs& p, int w, int lane) {
   constexpr int LOADS = Cfg<FMT>::LOADS, WAVES = Cfg<FMT>::WAVES;
-  LoadOffsets<FMT> o;
+  LoadOffsets<FMT, PAIRED> o;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int row = (i * WAVES + w) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(row);
     o.tile[i] = (uint32_t)(row * p.lda + c * 16);
+    if constexpr (PAIRED) o.btile[i] = (uint32_t)(paired_row(row, p.h) * p.lda + c * 16);
   }
-  o.scale = (uint32_t)((((w * 64) % BM) + lane) * p.ldsf);
+  const int srow = ((w * 64) % BM) + lane;
+  o.scale = (uint32_t)(srow * p.ldsf);
+  o.bscale = PAIRED ? (uint32_t)(paired_row(srow, p.h) * p.ldsf) : o.scale;
   return o;
 }
 
@@ -331,8 +355,8 @@ __device__ __forceinline__ LoadOffsets<FMT> make_offsets(const GemmArgs& p, int 
 // the step calls it ahead of its matrix instructions, because the branch on
 // the step's place in its scale group would otherwise let the compiler sink
 // the instructions before it below it and bunch up the operand loads.
-template <int FMT, bool GS>
-__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o, int k, uint32_t base,
+template <int FMT, bool GS, bool PAIRED>
+__device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT, PAIRED>& o, int k, uint32_t base,
                                       uint32_t lds0, int w, int part = -1, int slots = 1) {
   using C = Cfg<FMT>;
   using L = Lay<FMT, GS>;
@@ -348,7 +372,8 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o,
       if (part < 0 || part == i * slots / (2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      if (part < 0 || part == (LOADS + i) * slots / (2 * LOADS)) dma16(rb, o.tile[i], lb + i * WAVES * 1024);
+      if (part < 0 || part == (LOADS + i) * slots / (2 * LOADS))
+        dma16(rb, PAIRED ? o.btile[i] : o.tile[i], lb + i * WAVES * 1024);
   }
   // Scales.  With four waves wave w loads rows [64 w, 64 w + 64) of A and of
   // B; with eight, waves 0-3 those rows of A and waves 4-7 of B.
@@ -363,10 +388,10 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o,
     const __amdgpu_buffer_rsrc_t rsb = rsrc(tl.sb + ks, tl.sb_bytes - ks);
     if constexpr (C::SOPS == 2) {
       dma16(rsa, o.scale, lsa);
-      dma16(rsb, o.scale, lsb);
+      dma16(rsb, o.bscale, lsb);
     } else {
       const bool is_a = w * 64 < BM;
-      dma16(is_a ? rsa : rsb, o.scale, is_a ? lsa : lsb);
+      dma16(is_a ? rsa : rsb, is_a ? o.scale : o.bscale, is_a ? lsa : lsb);
     }
     return;
   }
@@ -380,14 +405,15 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT>& o,
 #pragma unroll
     for (int h = 0; h < C::PLANES; ++h) {
       dma4(rsa, o.scale + 4 * h, lsa + h * BM * 4);
-      dma4(rsb, o.scale + 4 * h, lsb + h * BN * 4);
+      dma4(rsb, o.bscale + 4 * h, lsb + h * BN * 4);
     }
   } else {
     const bool is_a = w * 64 < BM;
     const __amdgpu_buffer_rsrc_t rs = is_a ? rsa : rsb;
     const uint32_t ls = is_a ? lsa : lsb;
+    const uint32_t so = is_a ? o.scale : o.bscale;
 #pragma unroll
-    for (int h = 0; h < C::PLANES; ++h) dma4(rs, o.scale + 4 * h, ls + h * BM * 4);
+    for (int h = 0; h < C::PLANES; ++h) dma4(rs, so + 4 * h, ls + h * BM * 4);
   }
 }
 
@@ -414,20 +440,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
-// SPLIT: the launch has a K split (p.ksplit > 1) and the epilogue writes
-// FP32 partial tiles instead of the BF16 output (a separate instantiation, so
-// that the second epilogue costs the single-pass kernel no registers).
-template <int FMT, bool SPLIT, bool GS>
+// Epilogues (separate instantiations, so that one costs the others no
+// registers): kEpiBf16 writes the BF16 output; kEpiSplit (the launch has a
+// K split, p.ksplit > 1) writes FP32 partial tiles; kEpiSwiglu (MXFP8, p.h > 0,
+// PAIRED B rows) applies SwiGLU and the MXFP8 re-quant and writes codes and
+// scales of y instead of the gate|up output.
+constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2;
+
+template <int FMT, int EPI, bool GS>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
   using L = Lay<FMT, GS>;
   constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
-  constexpr int kStores = C::kStores;
+  // vector-memory operations of the epilogue (at least; the waits below rely
+  // on no fewer being issued after the next tile's loads)
+  constexpr int kStores = EPI == kEpiSwiglu ? FI * 2 * 3 : C::kStores;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TiledTable tt;
 
   const int G0 = p.num_groups;
-  const int NT = (int)((p.n + BN - 1) / BN);
+  constexpr bool PAIRED = EPI == kEpiSwiglu;
+  static_assert(!PAIRED || (FMT == 0 && Cfg<FMT>::FJ == 4), "the SwiGLU epilogue pairs fragments j and j + 2");
+  constexpr int TCOLS = PAIRED ? 128 : BN;                  // output columns per n-tile
+  const int NT = (int)(((PAIRED ? p.h : p.n) + TCOLS - 1) / TCOLS);
   const int mt_per = p.form == kUniform ? (int)((p.slot_rows + BM - 1) / BM) : 0;
   int total_gm, n_heavy = 0;
   if (p.form == kUniform) total_gm = G0 * mt_per;
@@ -456,7 +491,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   int t = tile_of(0);
   if (t >= total) return;
 
-  const LoadOffsets<FMT> lo = make_offsets<FMT>(p, w, lane);
+  const LoadOffsets<FMT, PAIRED> lo = make_offsets<FMT, PAIRED>(p, w, lane);
 
   // Fragment-read offsets.  Fragment row i of the wave tile is LDS row
   // 128 wm + 32 i + r32 (A) / 128 wn + 32 i + r32 (B); its swizzle is
@@ -666,12 +701,12 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
   };
 
-  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t, L::SPG);
+  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t, L::SPG, TCOLS);
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
-  issue<FMT, GS>(tl, lo, 0, smem_lds, smem_lds, w);
-  issue<FMT, GS>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
+  issue<FMT, GS, PAIRED>(tl, lo, 0, smem_lds, smem_lds, w);
+  issue<FMT, GS, PAIRED>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
   wait_vm<L::OPS1>();
   bar();
   // the scale words of step k of tile `tl` in stage `stage`
@@ -710,7 +745,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     for (int k = 1; k + 1 < tl.nk; ++k) {
       const uint32_t nxt = smem_lds + (st ^ 1) * L::STAGE;
       step(smem + st * L::STAGE, scl(tl, k, st),
-           [&](int part, int slots) { issue<FMT, GS>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
+           [&](int part, int slots) { issue<FMT, GS, PAIRED>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
            std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<0>();
@@ -722,17 +757,17 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     const bool has_next = t_next < total;
     Tile tn = tl;
     if (has_next) {
-      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG);
+      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG, TCOLS);
       // the scale buffer after this tile's last scale group
       tn.sg = (tl.sg + tl.nk / L::SPG) & 1;
-      issue<FMT, GS>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
+      issue<FMT, GS, PAIRED>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
     }
     step(smem + st * L::STAGE, scl(tl, tl.nk - 1, st), [](int, int) {}, std::false_type{});
     pin();
     bar();                            // stage `st` is free
-    if (has_next) issue<FMT, GS>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
+    if (has_next) issue<FMT, GS, PAIRED>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
 
-    if constexpr (SPLIT) {
+    if constexpr (EPI == kEpiSplit) {
       // ---- K-split epilogue: this slice's FP32 partial tile to
       // partial[slice][row][col], 16-byte buffer stores of 4 consecutive
       // columns (lane l, register 4b + r holds fragment row l % 32, column
@@ -758,6 +793,111 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
             __builtin_amdgcn_raw_buffer_store_b128(o, prsrc, (int)off, 0, 0);
           }
         }
+    } else if constexpr (EPI == kEpiSwiglu) {
+      // ---- SwiGLU + MXFP8 re-quant epilogue.  Fragment j < 2 of this wave
+      // holds gate and fragment j + 2 up of the same 32 y columns
+      // (ycol .. ycol + 31, one 32-group), in the same lanes and registers:
+      // lane l, register 4b + r is row l % 32, column 8b + 4(l/32) + r.  Each
+      // value gets the bias and the BF16 rounding of the gate|up output, then
+      // y = up * silu(gate) and the quantiser of hq_group_wise_quant -- the
+      // same instructions as the separate GEMM and SwiGLU kernels, so the
+      // codes are the same.  Rows at or past the group's valid rows fall
+      // outside the store descriptors.
+      const int64_t H = p.h;
+      const int64_t vrows = tl.vend > tl.row0 ? tl.vend - tl.row0 : 0;
+      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(uniform_ptr(p.q_out + tl.row0 * H)), (short)0,
+          (int)ufirst((uint32_t)(vrows * H)), 0x00020000);
+      const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(uniform_ptr(p.sf_out + tl.row0 * (H / 32))), (short)0,
+          (int)ufirst((uint32_t)(vrows * (H / 32))), 0x00020000);
+      const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
+      // lane-derived offsets from an opaque copy of the lane id, so that the
+      // compiler computes them here instead of keeping them live through the
+      // K loop (which runs out of registers)
+      int le;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(le) : "v"(lane));
+      const int he = le >> 5, re = le & 31;
+      const uint32_t H32 = (uint32_t)H;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t ycol = tl.n0 + wn * 64 + 32 * j;          // the 32-group's first column
+        // this lane's gate and up bias of the fragment pair's columns
+        float gb[4][4], ub[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int64_t col = ycol + 8 * b + 4 * he;
+          uint2 bg = make_uint2(0u, 0u), bu = make_uint2(0u, 0u);
+          if (bias != nullptr) {
+            bg = *reinterpret_cast<const uint2*>(bias + col);
+            bu = *reinterpret_cast<const uint2*>(bias + H + col);
+          }
+          gb[b][0] = bf16_lo(bg.x); gb[b][1] = bf16_hi(bg.x); gb[b][2] = bf16_lo(bg.y); gb[b][3] = bf16_hi(bg.y);
+          ub[b][0] = bf16_lo(bu.x); ub[b][1] = bf16_hi(bu.x); ub[b][2] = bf16_lo(bu.y); ub[b][3] = bf16_hi(bu.y);
+        }
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+          const uint32_t mr = (uint32_t)(wm * WTM + i * 32 + re);   // row within the tile
+          float y[4][4];
+          uint32_t amax = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const uint32_t g2 = pack_bf16x2(acc[i][j][4 * b + r] + gb[b][r], acc[i][j][4 * b + r + 1] + gb[b][r + 1]);
+              const uint32_t u2 = pack_bf16x2(acc[i][j + 2][4 * b + r] + ub[b][r],
+                                              acc[i][j + 2][4 * b + r + 1] + ub[b][r + 1]);
+              y[b][r] = silu_mul(bf16_lo(g2), bf16_lo(u2));
+              y[b][r + 1] = silu_mul(bf16_hi(g2), bf16_hi(u2));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t a = __float_as_uint(y[b][r]) & 0x7fffffffu;
+              amax = a > amax ? a : amax;
+            }
+          }
+          // the other 16 columns of the group are in lane l ^ 32
+          const uint32_t other = (uint32_t)__shfl_xor((int)amax, 32, 64);
+          amax = other > amax ? other : amax;
+          const uint32_t sb = mx_scale_byte<8>(amax);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            // lanes l and l ^ 32 swap a quad: this lane's 8-column run
+            // ycol + 16e + 8(l/32) .. + 7
+            float run[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[2 * e][r]),
+                                                               __float_as_uint(y[2 * e + 1][r]), false, false);
+              run[r] = __uint_as_float(sw[0]);
+              run[4 + r] = __uint_as_float(sw[1]);
+            }
+            const uint2 codes = mx_fp8x8(run, sb);
+            const uint32_t c0 = (uint32_t)ycol + 16 * e + 8 * he;
+            typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{codes.x, codes.y}, qrs, (int)(mr * H32 + c0), 0, 0);
+            if (p.y_debug != nullptr) {
+              const uint8_t* ybase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.y_debug + tl.row0 * H));
+              const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+                  const_cast<uint8_t*>(ybase), (short)0, (int)ufirst((uint32_t)(vrows * H * 4)), 0x00020000);
+              typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+              const uint32_t yo = (mr * H32 + c0) * 4;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  v4u{__float_as_uint(run[0]), __float_as_uint(run[1]), __float_as_uint(run[2]), __float_as_uint(run[3])},
+                  yrs, (int)yo, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  v4u{__float_as_uint(run[4]), __float_as_uint(run[5]), __float_as_uint(run[6]), __float_as_uint(run[7])},
+                  yrs, (int)(yo + 16), 0, 0);
+            }
+          }
+          // the scale byte from lane group 0 (lane group 1's store takes the
+          // drop marker: one store instruction for the wave either way)
+          const uint32_t so = he == 0 ? mr * (H32 / 32) + (uint32_t)ycol / 32 : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, srs, (int)so, 0, 0);
+          // one 32-group at a time (interleaving the groups runs out of registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     } else {
       // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
       // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
@@ -909,10 +1049,10 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   static std::atomic<bool> attr_set[64];
   const bool cached = dev.device >= 0 && dev.device < 64;
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, false, GS>,
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiBf16, GS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, true, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiSplit, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               smem);
     if (e != hipSuccess) return e;
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
@@ -970,14 +1110,14 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
         q1.ksplit = 1;
         q1.partial = nullptr;
         q1.tile_limit = (int32_t)(tiles - cols * mb);
-        hipLaunchKernelGGL((mx_gemm_tiled<FMT, false, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
+        hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
                            s, q1);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess) {
           int64_t g2 = cols * mb * S;
           if (g2 > grid_full) g2 = grid_full;
           if (g2 >= 8) g2 -= g2 % 8;
-          hipLaunchKernelGGL((mx_gemm_tiled<FMT, true, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
+          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
           e = hipGetLastError();
         }
         if (e == hipSuccess) {
@@ -1018,9 +1158,9 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
   if (q.ksplit > 1)
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, true, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   else
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, false, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   hipError_t e = hipGetLastError();
   if (q.ksplit > 1) {
     if (e == hipSuccess) {
@@ -1035,7 +1175,46 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   return e;
 }
 
+// The gate|up GEMM with the SwiGLU + re-quant epilogue: grouped-contiguous
+// MXFP8, h / 128 n-tiles of 128 gate + 128 up weight rows each.
+template <bool GS>
+hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  const int smem = Lay<0, GS>::SMEM;
+  static std::atomic<bool> attr_set[64];
+  const bool cached = dev.device >= 0 && dev.device < 64;
+  if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<0, kEpiSwiglu, GS>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    if (cached) attr_set[dev.device].store(true, std::memory_order_release);
+  }
+  const int64_t tiles = ((p.m_rows + BM - 1) / BM + p.num_groups) * (p.h / 128);
+  int cus = dev.num_cus;
+  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+  int64_t grid = cus;
+  if (tiles < grid) grid = tiles;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  GemmArgs q = p;
+  q.ksplit = 1;
+  q.partial = nullptr;
+  q.tile_limit = 0;
+  hipLaunchKernelGGL((mx_gemm_tiled<0, kEpiSwiglu, GS>), dim3((unsigned)grid), dim3(Cfg<0>::THREADS), smem, s, q);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool tiled_supported(const GemmArgs& p);
+
+bool gemm_swiglu_supported(const GemmArgs& p) {
+  return p.mode == kMXFP8 && p.form == kContiguous && p.h > 0 && p.h % 128 == 0 && p.n == 2 * p.h &&
+         tiled_supported(p);
+}
+
+hipError_t launch_gemm_swiglu(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  return p.ldsf % 16 == 0 ? launch_swiglu_cfg<true>(s, p, dev) : launch_swiglu_cfg<false>(s, p, dev);
+}
 
 bool tiled_supported(const GemmArgs& p) {
   const int64_t step = p.mode == kMXFP8 ? 128 : 256;

@@ -231,6 +231,46 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
   return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
 }
 
+hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode, const uint8_t* a,
+                                                const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                                const int32_t* group_end, int32_t num_groups,
+                                                const int32_t* valid, const uint16_t* bias, uint8_t* q,
+                                                uint8_t* sf, float* y_debug, int64_t m_total, int64_t h,
+                                                int64_t k, int32_t cu_limit) {
+  const char* what = "hq_group_contiguous_gemm_swiglu_quant";
+  if (mode != HQ_MXFP8) return fail(HQ_ERR_MODE, "%s: only MXFP8 is supported (got %d)", what, mode);
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  if (h <= 0 || h % 128 != 0 || h > (1 << 20))
+    return fail(HQ_ERR_SHAPE, "%s: h=%lld must be a positive multiple of 128, at most 2^20", what, (long long)h);
+  GemmCheck c{mode, a, sfa, b, sfb, bias, nullptr, q, m_total, 2 * h, k, num_groups, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  if (!group_end || !sf) return fail(HQ_ERR_NULL, "%s: group_end and sf are required", what);
+  if (y_debug && !aligned16(y_debug)) return fail(HQ_ERR_ALIGN, "%s: y_debug must be 16-byte aligned", what);
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, nullptr, nullptr, 2 * h, k, cu_limit);
+  p.form = hq::kContiguous;
+  p.group_end = group_end;
+  p.num_groups = num_groups;
+  p.m_rows = m_total;
+  p.slot_rows = 0;
+  p.h = h;
+  p.q_out = q;
+  p.sf_out = sf;
+  p.y_debug = y_debug;
+  p.valid = valid;
+  if (!hq::gemm_swiglu_supported(p)) {
+    if ((reinterpret_cast<uintptr_t>(sfa) | reinterpret_cast<uintptr_t>(sfb)) & 3)
+      return fail(HQ_ERR_ALIGN, "%s: sfa and sfb must be 4-byte aligned", what);
+    return fail(HQ_ERR_SHAPE, "%s: k=%lld must be a multiple of 128 of at least 256", what, (long long)k);
+  }
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  return launched(hq::launch_gemm_swiglu((hipStream_t)stream, p, dev), what);
+}
+
 hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
                                const uint8_t* b, const uint8_t* sfb, const int32_t* masked_m,
                                int32_t num_groups, int64_t max_m_per_group, const uint16_t* bias,

@@ -48,6 +48,16 @@ struct GemmArgs {
   float* partial;
   int64_t ldo;          // output row stride in elements (0: n); the K-split reduce only
   int32_t tile_limit;   // tiled kernel: process only the first tile_limit tiles (0: all)
+  // h > 0: gate|up GEMM whose epilogue applies SwiGLU and the MXFP8 re-quant
+  // (tiled kernel, grouped-contiguous form): the weights hold n = 2h rows
+  // [gate | up]; y = up * silu(gate) of the first valid[g] rows of each group
+  // goes to q_out [m_rows, h] / sf_out [m_rows, h/32] (and y_debug
+  // [m_rows, h] FP32 when given); out is not written.
+  int64_t h;
+  uint8_t* q_out;
+  uint8_t* sf_out;
+  float* y_debug;
+  const int32_t* valid;
 };
 
 struct DeviceInfo {
@@ -64,6 +74,10 @@ hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64
                                int64_t slot_rows, const int32_t* valid, uint8_t* q,
                                uint8_t* sf, const float* gs, float* y_debug);
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
+// The gate|up GEMM with the SwiGLU + re-quant epilogue (args.h > 0); false
+// when the tiled kernel cannot take the shape (K, alignment).
+bool gemm_swiglu_supported(const GemmArgs& args);
+hipError_t launch_gemm_swiglu(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
 hipError_t launch_permute(hipStream_t s, const uint8_t* x, int64_t tokens, int64_t row_bytes,
                           int64_t hidden, const void* scale, int32_t scale_mode, const int64_t* ids,
                           int32_t topk, int32_t experts, int64_t max_tokens, uint8_t* out_x,

@@ -22,13 +22,6 @@ struct Y8 {
   float f[8];
 };
 
-__device__ __forceinline__ float silu_mul(float gate, float up) {
-  // exp(-gate) through the hardware exp2; 1/(1+e) through the hardware
-  // reciprocal.  Large negative gates give e = +Inf and y = 0.
-  float e = __builtin_amdgcn_exp2f(-gate * 1.4426950408889634f);
-  return up * gate * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 template <int MODE>
 __device__ __forceinline__ void emit(const Y8& y, int64_t row, int64_t chunk, int64_t h,
                                      uint8_t* __restrict__ q, uint8_t* __restrict__ sf,

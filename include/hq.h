@@ -162,6 +162,36 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode,
                                    int32_t cu_limit);
 
 /*
+ * Grouped-contiguous gate|up GEMM with the SwiGLU + re-quantisation applied in
+ * its epilogue (HALOps "GEMM" page, group_contiguous_gemm and
+ * fused_swiglu_quant sections; the flashrt/fp4-gemm page's fused GEMM
+ * epilogues).  The result is that of hq_group_contiguous_gemm into a BF16
+ * [m_total, 2h] x = [gate | up] followed by hq_fused_swiglu_quant(MXFP8,
+ * group_end, valid) on x -- the same codes and scales, bit for bit (x's BF16
+ * rounding included) -- without writing or reading x.
+ *   mode must be HQ_MXFP8.  a [m_total, k], sfa [m_total, k/32],
+ *   b [num_groups, 2h, k] (rows [0, h) gate, [h, 2h) up), sfb
+ *   [num_groups, 2h, k/32], group_end [num_groups] int32 (device, as for
+ *   hq_group_contiguous_gemm), valid (optional, device int32 [num_groups]:
+ *   only the first min(valid[g], size) rows of group g are written),
+ *   bias (optional) [num_groups, 2h] BF16, q [m_total, h] E4M3 codes,
+ *   sf [m_total, h/32] UE8M0, y_debug (optional, device float [m_total, h]):
+ *   the FP32 y of the written rows.
+ *   h % 128 == 0 (h <= 2^20); k % 128 == 0 and k >= 256 (the tiled kernel's
+ *   K step and two steps); sfa / sfb 4-byte aligned.
+ * Rows not written keep their contents.  No workspace is allocated.
+ */
+hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode,
+                                                const uint8_t* a, const uint8_t* sfa,
+                                                const uint8_t* b, const uint8_t* sfb,
+                                                const int32_t* group_end,
+                                                int32_t num_groups, const int32_t* valid,
+                                                const uint16_t* bias, uint8_t* q,
+                                                uint8_t* sf, float* y_debug,
+                                                int64_t m_total, int64_t h, int64_t k,
+                                                int32_t cu_limit);
+
+/*
  * Grouped-masked GEMM (HALOps "GEMM" page, group_masked_gemm section): expert
  * e owns the slot of rows [e * max_m, (e + 1) * max_m); only its first
  * min(masked_m[e], max_m) rows are computed and written (padded rows are
