@@ -5,8 +5,11 @@ Default workload (one "step" = one pass of the MoE expert forward hot path):
   counts ~ Multinomial(65536, Dirichlet(1)), each group padded to a multiple
   of 128 rows (cumulative int32 ends); K = 4096, gate|up N = 2 x 1536.
     1. hq_group_wise_quant     MXFP8 quantisation of the [R, 4096] activations
-    2. hq_group_contiguous_gemm  [R, 4096] x [32, 3072, 4096]^T -> BF16 [R, 3072]
-    3. hq_fused_swiglu_quant   y = up * silu(gate) on the valid rows -> MXFP8
+    2. hq_group_contiguous_gemm_swiglu_quant  [R, 4096] x [32, 3072, 4096]^T with
+       y = up * silu(gate) of the valid rows re-quantised to MXFP8 in the
+       GEMM's epilogue (--workload moe_unfused: hq_group_contiguous_gemm to
+       BF16 [R, 3072], then hq_fused_swiglu_quant; the per-kernel pass also
+       times these two calls beside the fused one)
   Weights are quantised once before timing (they are static parameters).
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
@@ -14,7 +17,8 @@ of the valid rows per second), the per-kernel times, the roofline of the
 dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
 and the oracle timed on a bounded sample on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload moe|moe_mlp|dense_fp4|masked_fp4|permute]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload moe|moe_unfused|moe_mlp|dense_fp4|masked_fp4|permute]
     python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
                                         # one JSON line per case
 """
@@ -82,11 +86,13 @@ def _traffic(kernel_key):
 
 
 # ---------------------------------------------------------------- MoE workload
-def run_moe(args, torch, hq, synth, down=False):
+def run_moe(args, torch, hq, synth, down=False, fused=False):
     """The MoE expert forward step: MXFP8 quantisation of the routed
     activations, the grouped gate|up GEMM, the fused SwiGLU + MXFP8 re-quant;
     with down=True also the down-projection grouped GEMM (K = H = 1536,
-    N = hidden = 4096) on the SwiGLU codes -- the whole expert MLP."""
+    N = hidden = 4096) on the SwiGLU codes -- the whole expert MLP; with
+    fused=True the gate|up GEMM applies SwiGLU + re-quant in its epilogue
+    (one call instead of two, no BF16 [rows, 3072] intermediate)."""
     dev = torch.device("cuda:0")
     log("generating MoE inputs (E=32, 65536 routed rows, K=4096, N=3072)")
     d = synth.moe_contiguous(threads=16)
@@ -122,13 +128,20 @@ def run_moe(args, torch, hq, synth, down=False):
         f2 = lambda: hq.hq_group_contiguous_gemm("mxfp8", aq, asf, wq, wsf, ge, out)
         f3 = lambda: hq.hq_fused_swiglu_quant("mxfp8", out, yq, ysf, E, ge, 0, valid)
         f4 = lambda: hq.hq_group_contiguous_gemm("mxfp8", yq, ysf, w2q, w2sf, ge, out2)
+        f5 = lambda: hq.hq_group_contiguous_gemm_swiglu_quant("mxfp8", aq, asf, wq, wsf, ge, yq, ysf,
+                                                              valid=valid)
         if t is None:
-            f1(); f2(); f3()
+            if fused:
+                f1(); f5()
+            else:
+                f1(); f2(); f3()
             if down:
                 f4()
         else:
             t.mark("quant", f1)
-            t.mark("gemm", f2)
+            if fused:
+                t.mark("gemm_swiglu", f5)
+            t.mark("gemm", f2)           # the two-call form, reported beside the fused one
             t.mark("swiglu", f3)
             if down:
                 t.mark("down", f4)
@@ -152,21 +165,31 @@ def run_moe(args, torch, hq, synth, down=False):
     flops = 2.0 * T * N * K
     quant_bytes = R * K * (2 + 1 + 1 / 32)     # the whole padded activation buffer
     swiglu_bytes = T * H * (4 + 1 + 1 / 32)
-    gemm_ms = timer.mean_ms("gemm")
     quant_ms = timer.mean_ms("quant")
     sw_ms = timer.mean_ms("swiglu")
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     kernels = {
         "quant_mxfp8": {"ms": quant_ms, "GB/s": quant_bytes / (quant_ms * 1e-3) / 1e9,
                         "frac_hbm": quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "traffic": _traffic("quant_mxfp8")},
-        "grouped_gemm_mxfp8": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
-                               "frac_mfma": gemm_tflops / PEAK_TFLOPS["mxfp8"]},
-        "swiglu_quant_mxfp8": {"ms": sw_ms, "GB/s": swiglu_bytes / (sw_ms * 1e-3) / 1e9,
-                               "frac_hbm": swiglu_bytes / (sw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                               "traffic": _traffic("swiglu_quant_mxfp8")},
     }
-    cfg = {"workload": "moe_grouped_contiguous_mxfp8_E32_T65536_K4096_N3072_swiglu",
+    gkeys = [("gemm_swiglu", "grouped_gemm_swiglu_mxfp8")] if fused else []
+    gkeys.append(("gemm", "grouped_gemm_mxfp8"))
+    for ev, key in gkeys:
+        g_ms = timer.mean_ms(ev)
+        g_tf = flops / (g_ms * 1e-3) / 1e12
+        kernels[key] = {"ms": g_ms, "TFLOP/s": g_tf, "frac_mfma": g_tf / PEAK_TFLOPS["mxfp8"],
+                        "traffic": _traffic(key)}
+    kernels["swiglu_quant_mxfp8"] = {"ms": sw_ms, "GB/s": swiglu_bytes / (sw_ms * 1e-3) / 1e9,
+                                     "frac_hbm": swiglu_bytes / (sw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                     "traffic": _traffic("swiglu_quant_mxfp8")}
+    if fused:
+        kernels["grouped_gemm_mxfp8"]["note"] = "two-call form, timed beside the step"
+        kernels["swiglu_quant_mxfp8"]["note"] = "two-call form, timed beside the step"
+    gkey = gkeys[0][1]                  # the step's GEMM: the roofline's kernel
+    gemm_ms = kernels[gkey]["ms"]
+    gemm_tflops = kernels[gkey]["TFLOP/s"]
+    cfg = {"workload": "moe_grouped_contiguous_mxfp8_E32_T65536_K4096_N3072_swiglu"
+                       + ("_fused_epilogue" if fused else ""),
            "experts": E, "routed_rows": T, "padded_rows": R, "k": K, "n": N, "h": H,
            "group_align": 128}
     if down:
@@ -177,8 +200,8 @@ def run_moe(args, torch, hq, synth, down=False):
         cfg = dict(cfg, workload="moe_mlp_mxfp8_E32_T65536_K4096_H1536_hidden4096", hidden=HID)
     roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_TFLOPS["mxfp8"],
             "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_TFLOPS["mxfp8"],
-            "traffic": _traffic("grouped_gemm_mxfp8"),
-            "kernel": "grouped_gemm_mxfp8", "flop_per_launch": flops}
+            "traffic": _traffic(gkey),
+            "kernel": gkey, "flop_per_launch": flops}
     step_flops = flops + (down_flops if down else 0.0)
     value = step_flops / (ms_step * 1e-3) / 1e12
     ctx = None if down else {"counts": counts, "ends": ends, "a": d["a"], "b": d["b"], "K": K, "N": N, "H": H}
@@ -434,7 +457,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe", choices=["moe", "moe_mlp", "dense_fp4", "masked_fp4", "permute", "sweep"])
+    ap.add_argument("--workload", default="moe", choices=["moe", "moe_unfused", "moe_mlp", "dense_fp4",
+                                                       "masked_fp4", "permute", "sweep"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
@@ -472,9 +496,9 @@ def main():
     if args.workload == "sweep":
         run_sweep(args, torch, hq, synth)
         return
-    runner = {"moe": run_moe, "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4,
-              "permute": run_permute,
-              "moe_mlp": lambda *a: run_moe(*a, down=True)}[args.workload]
+    runner = {"moe": lambda *a: run_moe(*a, fused=True), "moe_unfused": run_moe,
+              "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4, "permute": run_permute,
+              "moe_mlp": lambda *a: run_moe(*a, down=True, fused=True)}[args.workload]
     res = runner(args, torch, hq, synth)
     value, ms_step, cfg, roof, kernels, ctx = res[:6]
     unit = res[6] if len(res) > 6 else "TFLOP/s"
@@ -493,7 +517,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"moe": "mxfp8", "moe_mlp": "mxfp8", "permute": "bf16"}.get(args.workload, args.mode),
+        "dtype": {"moe": "mxfp8", "moe_mlp": "mxfp8", "moe_unfused": "mxfp8",
+                  "permute": "bf16"}.get(args.workload, args.mode),
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,
