@@ -19,7 +19,7 @@ __all__ = [
     "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
-    "hq_group_contiguous_gemm_swiglu_quant",
+    "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
     "HQ_SCALE_BROADCAST", "HQ_SCALE_DIRECT",
     "hq_last_error", "library_path", "load", "EXPORTED_SYMBOLS",
@@ -39,7 +39,8 @@ MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
 EXPORTED_SYMBOLS = (
     "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
-    "hq_group_contiguous_gemm_swiglu_quant", "hq_prefill_permute_to_masked_gemm",
+    "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
+    "hq_prefill_permute_to_masked_gemm",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,8 @@ _SIGS = {
     "hq_batch_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                   _I64, _I64, _I64, _I32], _I32),
+    "hq_group_contiguous_gemm_ptr_array": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
+                                            _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm_swiglu_quant": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP,
                                                _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_group_masked_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _VP, _VP, _VP,
@@ -202,6 +205,39 @@ def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, al
     _check(load().hq_group_contiguous_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
                                            _p(group_end), E, _p(bias), _p(alpha), _p(out),
                                            rows, n, k, cu_limit))
+
+
+def hq_group_contiguous_gemm_ptr_array(mode, a, sfa, bs, sfbs, group_end, out, n, bias=None,
+                                       alpha=None, cu_limit=0):
+    """Grouped-contiguous GEMM whose group g uses the separate weight tensors
+    bs[g] [n, K'] and sfbs[g] [n, k/gs] (uint8, contiguous, 16-byte aligned):
+    the binding builds the device arrays of their addresses."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    E = len(bs)
+    if len(sfbs) != E:
+        raise ValueError("bs and sfbs must have one tensor per group")
+    for g in range(E):
+        _need(bs[g], f"bs[{g}]", torch.uint8, n * code_cols(mode, k))
+        _need(sfbs[g], f"sfbs[{g}]", torch.uint8, n * (k // group_size(mode)))
+        if not bs[g].is_contiguous() or not sfbs[g].is_contiguous():
+            raise ValueError(f"bs[{g}] and sfbs[{g}] must be contiguous")
+        if bs[g].data_ptr() % 16 or sfbs[g].data_ptr() % 16:
+            raise ValueError(f"bs[{g}] and sfbs[{g}] must be 16-byte aligned")
+    _need(a, "a", torch.uint8, rows * code_cols(mode, k))
+    _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
+    _need(group_end, "group_end", torch.int32, E)
+    _need(out, "out", torch.bfloat16, rows * n)
+    _need(bias, "bias", torch.bfloat16, E * n)
+    _need(alpha, "alpha", torch.float32, E)
+    dev = a.device
+    bp = torch.tensor([t.data_ptr() for t in bs], dtype=torch.int64).to(dev, non_blocking=False)
+    sp = torch.tensor([t.data_ptr() for t in sfbs], dtype=torch.int64).to(dev, non_blocking=False)
+    _check(load().hq_group_contiguous_gemm_ptr_array(_stream(a), mode, _p(a), _p(sfa), _p(bp), _p(sp),
+                                                     _p(group_end), E, _p(bias), _p(alpha), _p(out),
+                                                     rows, n, k, cu_limit))
+    return bp, sp     # keep the address arrays alive until the stream has run the call
 
 
 def hq_group_contiguous_gemm_swiglu_quant(mode, a, sfa, b, sfb, group_end, q, sf, valid=None,

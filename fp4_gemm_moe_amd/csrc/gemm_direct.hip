@@ -152,8 +152,10 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
       arow[fm] = p.a + r * p.lda;
       asf[fm] = p.sfa + r * p.ldsf;
     }
-    const uint8_t* bg = p.b + (int64_t)tr.g * p.b_stride;
-    const uint8_t* bsg = p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g])
+                                 : p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g])
+                                    : p.sfb + (int64_t)tr.g * p.sfb_stride;
     const uint8_t* brow[FN];
     const uint8_t* bsf[FN];
 #pragma unroll
@@ -316,8 +318,10 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
       arow[fm] = p.a + r * p.lda;
       asf[fm] = p.sfa + r * p.ldsf;
     }
-    const uint8_t* bg = p.b + (int64_t)tr.g * p.b_stride;
-    const uint8_t* bsg = p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g])
+                                 : p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g])
+                                    : p.sfb + (int64_t)tr.g * p.sfb_stride;
     const uint8_t* brow[FN];
     const uint8_t* bsf[FN];
 #pragma unroll

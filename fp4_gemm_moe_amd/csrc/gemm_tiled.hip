@@ -292,12 +292,16 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
     if (gs + c < tl.vend) tl.vend = ufirst64(gs + c);
   }
   tl.n0 = (int64_t)nt * tile_cols;
-  const int64_t brow0 = (int64_t)tl.g * p.n + tl.n0;          // first weight row
-  const int64_t brows = (int64_t)p.num_groups * p.n;
+  // the group's weights: one tensor of all groups, or its own allocation
+  const bool discrete = p.b_ptrs != nullptr;
+  const uint8_t* bbase = discrete ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tl.g]) : p.b;
+  const uint8_t* sbbase = discrete ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tl.g]) : p.sfb;
+  const int64_t brow0 = (discrete ? 0 : (int64_t)tl.g * p.n) + tl.n0;   // first weight row
+  const int64_t brows = discrete ? p.n : (int64_t)p.num_groups * p.n;
   tl.a = uniform_ptr(p.a + tl.row0 * p.lda + kb);
-  tl.b = uniform_ptr(p.b + brow0 * p.lda + kb);
+  tl.b = uniform_ptr(bbase + brow0 * p.lda + kb);
   tl.sa = uniform_ptr(p.sfa + tl.row0 * p.ldsf + ksb);
-  tl.sb = uniform_ptr(p.sfb + brow0 * p.ldsf + ksb);
+  tl.sb = uniform_ptr(sbbase + brow0 * p.ldsf + ksb);
   // A rows past the tile's valid rows (the next group's, or a masked slot's
   // padding) are not fetched: the bounded loads fill them with zeros.
   // Extents count from the slice's first K byte.

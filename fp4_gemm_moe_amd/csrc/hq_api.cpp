@@ -231,6 +231,36 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
   return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
 }
 
+hq_status hq_group_contiguous_gemm_ptr_array(void* stream, int32_t mode, const uint8_t* a,
+                                             const uint8_t* sfa, const uint64_t* b_ptrs,
+                                             const uint64_t* sfb_ptrs, const int32_t* group_end,
+                                             int32_t num_groups, const uint16_t* bias,
+                                             const float* alpha, uint16_t* out, int64_t m_total,
+                                             int64_t n, int64_t k, int32_t cu_limit) {
+  const char* what = "hq_group_contiguous_gemm_ptr_array";
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  // b / sfb stand in for the pointer arrays in the common checks (their
+  // elements' alignment is the caller's contract: the arrays are device data)
+  GemmCheck c{mode, a, sfa, b_ptrs, sfb_ptrs, bias, alpha, out, m_total, n, k, num_groups, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  if (!group_end) return fail(HQ_ERR_NULL, "%s: group_end is required", what);
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, nullptr, nullptr, bias, alpha, out, n, k, cu_limit);
+  p.form = hq::kContiguous;
+  p.group_end = group_end;
+  p.num_groups = num_groups;
+  p.m_rows = m_total;
+  p.slot_rows = 0;
+  p.b_ptrs = b_ptrs;
+  p.sfb_ptrs = sfb_ptrs;
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
+}
+
 hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode, const uint8_t* a,
                                                 const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
                                                 const int32_t* group_end, int32_t num_groups,

@@ -58,6 +58,11 @@ struct GemmArgs {
   uint8_t* sf_out;
   float* y_debug;
   const int32_t* valid;
+  // Discrete expert weights (grouped forms): b_ptrs[g] / sfb_ptrs[g] are the
+  // device addresses of group g's [n, K'] codes and [n, k/gs] scales; b / sfb
+  // and the strides are then unused.  nullptr: one [groups, n, K'] tensor.
+  const uint64_t* b_ptrs;
+  const uint64_t* sfb_ptrs;
 };
 
 struct DeviceInfo {

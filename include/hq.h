@@ -162,6 +162,30 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode,
                                    int32_t cu_limit);
 
 /*
+ * Grouped-contiguous GEMM with discrete expert weights (cuDNN FE "Grouped GEMM
+ * + dGLU (SM100)" page, the discrete b_ptrs form of its B operand): as
+ * hq_group_contiguous_gemm, but group g's weights live in their own
+ * allocations.
+ *   b_ptrs [num_groups], sfb_ptrs [num_groups]: device arrays of 64-bit
+ *   device addresses; b_ptrs[g] points to group g's [n, K'] codes and
+ *   sfb_ptrs[g] to its [n, k/gs] scales (row-major, as b[g] / sfb[g] of
+ *   hq_group_contiguous_gemm).  Every code address must be 16-byte aligned
+ *   and every scale address 16-byte aligned (device data: not checked).
+ *   Other arguments and the result as for hq_group_contiguous_gemm; the
+ *   arrays and what they point to are read on the stream, so they must stay
+ *   alive and unchanged until the call's work has run.
+ */
+hq_status hq_group_contiguous_gemm_ptr_array(void* stream, int32_t mode,
+                                             const uint8_t* a, const uint8_t* sfa,
+                                             const uint64_t* b_ptrs,
+                                             const uint64_t* sfb_ptrs,
+                                             const int32_t* group_end,
+                                             int32_t num_groups, const uint16_t* bias,
+                                             const float* alpha, uint16_t* out,
+                                             int64_t m_total, int64_t n, int64_t k,
+                                             int32_t cu_limit);
+
+/*
  * Grouped-contiguous gate|up GEMM with the SwiGLU + re-quantisation applied in
  * its epilogue (HALOps "GEMM" page, group_contiguous_gemm and
  * fused_swiglu_quant sections; the flashrt/fp4-gemm page's fused GEMM
