@@ -143,6 +143,21 @@ def bf16_decode(bits):
         return b.view(np.float32).astype(np.float64)
 
 
+def fp16_decode(bits):
+    """IEEE binary16 bit patterns (uint16) -> float64, from the fields: sign
+    bit 15, exponent bits 10-14 (bias 15), fraction bits 0-9; exponent 0 is
+    +-fraction * 2^-24 (zero and subnormals), exponent 31 is Inf (fraction 0)
+    or NaN.  (Input dtype of the HALOps "GEMM" page's group_wise_quant.)"""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = sign * (1.0 + f / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = sign * f * 2.0 ** -24
+    special = np.where(f == 0, sign * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 31, special, normal))
+
+
 def bf16_round(x):
     """float64 -> BF16 bits, one rounding (nearest, ties to even).
 

@@ -72,6 +72,11 @@ def mx_quant_bf16(x_bits, fmt):
     return mx_quant_values(F.bf16_decode(x_bits), fmt)
 
 
+def mx_quant_fp16(x_bits, fmt):
+    """MX quantisation of FP16 rows given as uint16 bit patterns."""
+    return mx_quant_values(F.fp16_decode(x_bits), fmt)
+
+
 def nvfp4_global_scale(amax_tensor):
     """g = fp32(amax / 2688), or 1 when amax == 0 (FP32 arithmetic)."""
     a = np.float32(amax_tensor)
@@ -108,6 +113,10 @@ def nvfp4_quant_values(x, g=None):
 
 def nvfp4_quant_bf16(x_bits, g=None):
     return nvfp4_quant_values(F.bf16_decode(x_bits), g)
+
+
+def nvfp4_quant_fp16(x_bits, g=None):
+    return nvfp4_quant_values(F.fp16_decode(x_bits), g)
 
 
 def dequant(codes, sf, fmt, g=None):

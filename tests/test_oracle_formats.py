@@ -127,6 +127,20 @@ def test_bf16_decode_all_patterns_matches_torch():
     assert np.array_equal(np.signbit(ref[fin]), np.signbit(ours[fin]))
 
 
+def test_fp16_decode_all_patterns_matches_numpy_and_torch():
+    # every binary16 pattern against numpy's and torch's own float16 decoders
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = F.fp16_decode(bits)
+    ref_np = bits.view(np.float16).astype(np.float64)
+    ref_t = torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    nan = np.isnan(ref_np)
+    assert np.array_equal(np.isnan(ours), nan) and np.array_equal(np.isnan(ref_t), nan)
+    assert np.array_equal(ours[~nan], ref_np[~nan]) and np.array_equal(ours[~nan], ref_t[~nan])
+    # sign of zero, the largest finite value, the smallest subnormal
+    assert np.signbit(F.fp16_decode(np.uint16(0x8000))) and F.fp16_decode(np.uint16(0x8000)) == 0
+    assert F.fp16_decode(np.uint16(0x7BFF)) == 65504.0 and F.fp16_decode(np.uint16(0x0001)) == 2.0 ** -24
+
+
 def test_bf16_round_identity_and_midpoints():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = F.bf16_decode(bits)
