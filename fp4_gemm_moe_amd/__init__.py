@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQError",
+    "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQ_IN_FP16", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
@@ -30,6 +30,7 @@ HQ_MXFP8 = 0
 HQ_MXFP4 = 1
 HQ_NVFP4 = 2
 HQ_GS_INPUT = 1
+HQ_IN_FP16 = 2
 HQ_SCALE_BROADCAST = 0
 HQ_SCALE_DIRECT = 1
 
@@ -147,12 +148,15 @@ def _check(status):
 
 # ---------------------------------------------------------------- the six calls
 def hq_group_wise_quant(mode, x, q, sf, global_scale=None, flags=0):
-    """x [m, k] bf16 -> q [m, K'] uint8, sf [m, k/gs] uint8 (in place).
-    NVFP4: global_scale is a float32 [1] tensor (read with HQ_GS_INPUT, else
-    written)."""
+    """x [m, k] bf16 or float16 -> q [m, K'] uint8, sf [m, k/gs] uint8 (in
+    place; a float16 x sets HQ_IN_FP16).  NVFP4: global_scale is a float32 [1]
+    tensor (read with HQ_GS_INPUT, else written)."""
     mode = _mode(mode)
     m, k = x.shape
-    _need(x, "x", torch.bfloat16)
+    if x.dtype == torch.float16:
+        flags |= HQ_IN_FP16
+    else:
+        _need(x, "x", torch.bfloat16)
     _need(q, "q", torch.uint8, m * code_cols(mode, k))
     _need(sf, "sf", torch.uint8, m * (k // group_size(mode)))
     _need(global_scale, "global_scale", torch.float32, 1)

@@ -148,9 +148,9 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x, int
   if (m < 0 || m > kI32 || k > kI32) return fail(HQ_ERR_SHAPE, "%s: m=%lld out of range", what, (long long)m);
   if (mode != HQ_NVFP4) {
     if (global_scale != nullptr) return fail(HQ_ERR_MODE, "%s: global_scale is NVFP4 only", what);
-    if (flags != 0) return fail(HQ_ERR_MODE, "%s: flags are NVFP4 only", what);
+    if ((flags & ~HQ_IN_FP16) != 0) return fail(HQ_ERR_MODE, "%s: flags 0x%x: only HQ_IN_FP16 applies to MX modes", what, flags);
   } else {
-    if ((flags & ~HQ_GS_INPUT) != 0) return fail(HQ_ERR_MODE, "%s: unknown flags 0x%x", what, flags);
+    if ((flags & ~(HQ_GS_INPUT | HQ_IN_FP16)) != 0) return fail(HQ_ERR_MODE, "%s: unknown flags 0x%x", what, flags);
     if (global_scale == nullptr) return fail(HQ_ERR_NULL, "%s: NVFP4 needs global_scale", what);
   }
   if (m == 0) return ok();
@@ -160,7 +160,7 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x, int
   hq_status st = current_device(&dev);
   if (st != HQ_OK) return st;
   return launched(hq::launch_quant((hipStream_t)stream, mode, x, m, k, q, sf, global_scale,
-                                   (flags & HQ_GS_INPUT) != 0),
+                                   (flags & HQ_GS_INPUT) != 0, (flags & HQ_IN_FP16) != 0),
                   what);
 }
 

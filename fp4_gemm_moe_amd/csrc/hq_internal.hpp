@@ -72,8 +72,9 @@ struct DeviceInfo {
 };
 
 // Returns hipSuccess or the error of the launch.
+// x: BF16 bit patterns, or IEEE binary16 ones when fp16.
 hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
-                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input);
+                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input, bool fp16);
 hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64_t rows,
                                int64_t h, int32_t num_groups, const int32_t* group_end,
                                int64_t slot_rows, const int32_t* valid, uint8_t* q,

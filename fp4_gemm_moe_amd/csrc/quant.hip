@@ -26,12 +26,21 @@ struct Chunk8 {
   float f[8];
 };
 
+// Eight 16-bit inputs -> FP32 (exact): BF16 (F16 = false) or IEEE binary16
+// (F16 = true, the hardware half -> float conversion).
+__device__ __forceinline__ float f16_bits(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <bool F16>
 __device__ __forceinline__ Chunk8 unpack(uint4 v) {
   Chunk8 c;
-  c.f[0] = bf16_lo(v.x); c.f[1] = bf16_hi(v.x);
-  c.f[2] = bf16_lo(v.y); c.f[3] = bf16_hi(v.y);
-  c.f[4] = bf16_lo(v.z); c.f[5] = bf16_hi(v.z);
-  c.f[6] = bf16_lo(v.w); c.f[7] = bf16_hi(v.w);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c.f[2 * i] = F16 ? f16_bits(w[i] & 0xFFFFu) : bf16_lo(w[i]);
+    c.f[2 * i + 1] = F16 ? f16_bits(w[i] >> 16) : bf16_hi(w[i]);
+  }
   return c;
 }
 
@@ -60,7 +69,7 @@ __device__ __forceinline__ void mx_emit(const Chunk8& c, uint32_t amax, int64_t 
   if ((ci & 3) == 0) sf[ci >> 2] = (uint8_t)sb;
 }
 
-template <int MODE>
+template <int MODE, bool F16>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restrict__ x,
                                                             int64_t nchunks,
                                                             uint8_t* __restrict__ q,
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restr
       // nchunks % 4 == 0 and quads start at multiples of 4: a lane quad is
       // all in or all out.
       if (ci < nchunks) {
-        Chunk8 c = unpack(v[u]);
+        Chunk8 c = unpack<F16>(v[u]);
         uint32_t amax = quad_max_u32(abs_max_bits(c));
         mx_emit<MODE>(c, amax, ci, q, sf);
       }
@@ -99,6 +108,7 @@ __global__ void nv_amax_zero(uint32_t* acc) { *acc = 0u; }
 // kAmaxUnroll independent 16-byte loads per thread per iteration of a
 // grid-stride loop (measured faster here than walking blocks of consecutive
 // chunks, which needs many more workgroups and atomics).
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restrict__ x,
                                                            int64_t nchunks,
                                                            uint32_t* __restrict__ acc) {
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restri
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
-      const uint32_t a = abs_max_bits(unpack(v[u]));
+      const uint32_t a = abs_max_bits(unpack<F16>(v[u]));
       m = a > m ? a : m;
     }
   }
@@ -149,6 +159,7 @@ __device__ __forceinline__ void nv_emit(const Chunk8& c, uint32_t amax_bits, flo
   if ((ci & 1) == 0) sf[ci >> 1] = (uint8_t)sb;
 }
 
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint4* __restrict__ x,
                                                             int64_t nchunks,
                                                             uint8_t* __restrict__ q,
@@ -169,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant_kernel(const uint4* __restr
     for (int u = 0; u < kUnroll; ++u) {
       int64_t ci = base + u * kThreads;
       if (ci < nchunks) {
-        Chunk8 c = unpack(v[u]);
+        Chunk8 c = unpack<F16>(v[u]);
         uint32_t amax = pair_max_u32(abs_max_bits(c));
         nv_emit(c, amax, g, d, ci, q, sf);
       }
@@ -187,15 +198,17 @@ int grid_for(int64_t nchunks, int per_thread) {
 
 }  // namespace
 
-hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
-                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input) {
+namespace {
+template <bool F16>
+hipError_t launch_quant_t(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
+                          uint8_t* q, uint8_t* sf, float* gs, bool gs_input) {
   const int64_t nchunks = m * k / 8;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int grid = grid_for(nchunks, kUnroll);
   if (mode == kMXFP8) {
-    hipLaunchKernelGGL(mx_quant_kernel<kMXFP8>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
+    hipLaunchKernelGGL((mx_quant_kernel<kMXFP8, F16>), dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
   } else if (mode == kMXFP4) {
-    hipLaunchKernelGGL(mx_quant_kernel<kMXFP4>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
+    hipLaunchKernelGGL((mx_quant_kernel<kMXFP4, F16>), dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
   } else {
     if (!gs_input) {
       uint32_t* acc = reinterpret_cast<uint32_t*>(gs);
@@ -203,14 +216,21 @@ hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, i
       int64_t ablocks = (nchunks + (int64_t)kThreads * kAmaxUnroll - 1) / ((int64_t)kThreads * kAmaxUnroll);
       if (ablocks > 1024) ablocks = 1024;     // ~4 per CU: 1024 atomics at most
       if (ablocks < 1) ablocks = 1;
-      hipLaunchKernelGGL(nv_amax_kernel, dim3((unsigned)ablocks), dim3(kThreads), 0, s, xv,
+      hipLaunchKernelGGL(nv_amax_kernel<F16>, dim3((unsigned)ablocks), dim3(kThreads), 0, s, xv,
                          nchunks, acc);
       hipLaunchKernelGGL(nv_gs_finalize, dim3(1), dim3(1), 0, s, gs);
     }
-    hipLaunchKernelGGL(nv_quant_kernel, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf,
+    hipLaunchKernelGGL(nv_quant_kernel<F16>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf,
                        (const float*)gs);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_quant(hipStream_t s, int mode, const uint16_t* x, int64_t m, int64_t k,
+                        uint8_t* q, uint8_t* sf, float* gs, bool gs_input, bool fp16) {
+  return fp16 ? launch_quant_t<true>(s, mode, x, m, k, q, sf, gs, gs_input)
+              : launch_quant_t<false>(s, mode, x, m, k, q, sf, gs, gs_input);
 }
 
 }  // namespace hq

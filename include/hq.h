@@ -71,22 +71,24 @@ typedef int32_t hq_status;
 
 /* hq_group_wise_quant flags */
 #define HQ_GS_INPUT 1u /* NVFP4: read the global scale from *global_scale   */
+#define HQ_IN_FP16 2u  /* x holds IEEE binary16 (FP16) patterns, not BF16  */
 
 /* Thread-local description of the last error of this thread ("" if none). */
 const char* hq_last_error(void);
 
 /*
- * Group-wise quantisation of BF16 rows (HALOps "GEMM" page, group_wise_quant
- * section; here always with the plain row-major scale layout).
+ * Group-wise quantisation of BF16 or FP16 rows (HALOps "GEMM" page,
+ * group_wise_quant section; here always with the plain row-major scale
+ * layout).
  *
- *   x   [m, k] BF16                         (input)
+ *   x   [m, k] BF16, or FP16 with flags & HQ_IN_FP16   (input)
  *   q   [m, k] (MXFP8) or [m, k/2] (FP4)    (output codes)
  *   sf  [m, k/gs]                           (output scales)
  *
  * MX modes: per row and 32-group, s = clamp(floor(log2 amax) - emax, -127,
  * 127) with emax = 8 (E4M3) or 2 (E2M1); sf = s + 127; code = nearest element
  * of x / 2^s, ties to even, saturating to +-448 / +-6, sign kept (also for
- * zero).  global_scale must be NULL and flags 0.
+ * zero).  global_scale must be NULL and flags 0 or HQ_IN_FP16.
  *
  * NVFP4: g = amax(x) / 2688 in FP32 (1 if amax == 0), or *global_scale when
  * flags & HQ_GS_INPUT.  Per 16-group: sf = UE4M3(amax_b / (6 g)), then
@@ -94,6 +96,8 @@ const char* hq_last_error(void);
  * rounded to nearest even (code = +-0 when decode(sf) * g == 0).
  * global_scale (device float[1]) is required: read when HQ_GS_INPUT is set,
  * otherwise computed and written (the call then enqueues an amax pass).
+ * Inputs convert exactly to FP32 (both formats); the rules above then apply
+ * to those values.
  */
 hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x,
                               int64_t m, int64_t k, uint8_t* q, uint8_t* sf,

@@ -106,7 +106,8 @@ def test_quant_rejects(lib):
     assert q(None, 0, A, 4, 64, A, A, A, 0) == -4       # global scale is NVFP4-only
     assert q(None, 1, A, 4, 64, A, A, NUL, 1) == -4     # flags are NVFP4-only
     assert q(None, 2, A, 4, 64, A, A, NUL, 0) == -1     # NVFP4 needs a global scale
-    assert q(None, 2, A, 4, 64, A, A, A, 2) == -4       # unknown flag
+    assert q(None, 2, A, 4, 64, A, A, A, 4) == -4       # unknown flag
+    assert q(None, 0, A, 4, 64, A, A, NUL, 3) == -4     # HQ_GS_INPUT is NVFP4-only, also with HQ_IN_FP16
     assert q(None, 0, MIS, 4, 64, A, A, NUL, 0) == -3
     assert q(None, 0, NUL, 4, 64, A, A, NUL, 0) == -1
     assert q(None, 0, NUL, 0, 64, NUL, NUL, NUL, 0) == 0

@@ -106,6 +106,62 @@ def test_quant_nvfp4_every_bf16_value(g):
     _check("nvfp4", out, dev, g=g, what=f"all normal BF16, g={g:g}")
 
 
+def _check_fp16(mode, bits, dev, g=None, what=""):
+    """FP16 input (HQ_IN_FP16): the device codes / scales / global scale
+    against the oracle's quantisation of the decoded FP16 values."""
+    U.banner(f"quant fp16 {mode} {bits.shape} {what}")
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(dev)
+    gs = None if g is None else torch.tensor([g], dtype=torch.float32, device=dev)
+    q, sf, gout = hq.quantize(x, mode, gs)
+    torch.cuda.synchronize()
+    if mode == "nvfp4":
+        oc, os_, og = Q.nvfp4_quant_fp16(bits, None if g is None else np.float32(g))
+        assert np.float32(float(gout.cpu()[0])) == np.float32(og), (float(gout.cpu()[0]), og)
+    else:
+        oc, os_ = Q.mx_quant_fp16(bits, mode)
+    assert np.array_equal(U.host_u8(sf), os_), f"{mode} {what}: {np.sum(U.host_u8(sf) != os_)} scale bytes differ"
+    assert np.array_equal(U.host_u8(q), oc), f"{mode} {what}: {np.sum(U.host_u8(q) != oc)} code bytes differ"
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4"])
+def test_quant_every_fp16_value(mode):
+    """FP16 input: every finite binary16 pattern (subnormals and +-65504
+    included), shuffled into 32-groups."""
+    dev = U.require_gpu()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits[(bits & 0x7C00) != 0x7C00]
+    rng = np.random.default_rng(15)
+    out = np.concatenate([rng.permutation(vals) for _ in range(3)])
+    out = out[: (len(out) // 256) * 256].reshape(-1, 256)
+    _check_fp16(mode, np.ascontiguousarray(out), dev, what="all finite FP16")
+
+
+@pytest.mark.parametrize("g", [None, 2.0 ** -20, 0.0012345, 2.0 ** 20])
+def test_quant_nvfp4_every_fp16_value(g):
+    """FP16 input, NVFP4: every normal binary16 pattern of either sign,
+    sorted by magnitude into 16-groups and shuffled (as for BF16); the global
+    scale computed from the tensor's amax (None) or supplied."""
+    dev = U.require_gpu()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ex = bits & 0x7C00
+    vals = bits[(ex != 0x7C00) & (ex != 0)]
+    vals = vals[np.argsort(vals & 0x7FFF, kind="stable")]
+    vals = vals[: (len(vals) // 16) * 16].reshape(-1, 16)
+    rng = np.random.default_rng(300 if g is None else int(np.log2(g)) + 400)
+    vals = rng.permuted(vals, axis=1)[rng.permutation(len(vals))]
+    out = np.ascontiguousarray(vals.reshape(-1, 256)[: (vals.size // 256)])
+    _check_fp16("nvfp4", out, dev, g=g, what=f"all normal FP16, g={g}")
+
+
+def test_quant_fp16_gaussian_rows():
+    """FP16 input, N(0, 1) rows of the MoE width in the three modes."""
+    dev = U.require_gpu()
+    x = torch.randn(96, 4096, generator=torch.Generator().manual_seed(12)).to(torch.float16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    for mode in MODES:
+        _check_fp16(mode, bits, dev, what="gaussian")
+
+
 def test_quant_nvfp4_supplied_global_scale():
     dev = U.require_gpu()
     rng = np.random.default_rng(3)
