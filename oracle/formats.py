@@ -158,6 +158,25 @@ def fp16_decode(bits):
     return np.where(e == 0, sub, np.where(e == 31, special, normal))
 
 
+FP16_MAX = 65504.0
+
+
+def fp16_round(x):
+    """float64 -> IEEE binary16 bits, one rounding (nearest, ties to even):
+    11 significant bits for exponents >= -14, a fixed quantum of 2^-24 below
+    (subnormals); magnitudes that round above 65504 become Inf; NaN stays NaN
+    (the GEMM output dtype of the flashrt/fp4-gemm page's *_fp16 GEMMs)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e = np.frexp(x)
+        q = np.maximum(e.astype(np.int64) - 11, -24)
+        r = np.ldexp(np.rint(np.ldexp(x, -q)), q)   # np.rint: ties to even
+        r = np.where(np.abs(r) > FP16_MAX, np.copysign(np.inf, x), r)
+        r = np.where(np.isnan(x), np.nan, r)
+        r16 = r.astype(np.float16)                  # exact: r is a binary16 value
+    return r16.view(np.uint16)
+
+
 def bf16_round(x):
     """float64 -> BF16 bits, one rounding (nearest, ties to even).
 

@@ -41,15 +41,15 @@ def dense_f64(a_deq, b_deq, bias=None, alpha=None):
     return acc
 
 
-def dense_gemm(mode, a, sfa, b, sfb, bias=None, alpha=None):
-    """Dense scaled GEMM -> BF16 bits [M, N].
+def dense_gemm(mode, a, sfa, b, sfb, bias=None, alpha=None, out="bf16"):
+    """Dense scaled GEMM -> BF16 bits [M, N] (out="fp16": binary16 bits).
 
     a: codes [M, K'] (K' = K for mxfp8, K/2 packed for the FP4 modes);
     sfa: [M, K/gs]; b, sfb likewise for [N, K]; bias: BF16 bits [N] or None;
     alpha: FP32 scalar or None."""
     fmt = _mode_fmt(mode)
     acc = dense_f64(dequant(a, sfa, fmt), dequant(b, sfb, fmt), bias, alpha)
-    return F.bf16_round(acc)
+    return F.fp16_round(acc) if out == "fp16" else F.bf16_round(acc)
 
 
 def batch_gemm(mode, a, sfa, b, sfb, bias=None, alpha=None):

@@ -141,6 +141,24 @@ def test_fp16_decode_all_patterns_matches_numpy_and_torch():
     assert F.fp16_decode(np.uint16(0x7BFF)) == 65504.0 and F.fp16_decode(np.uint16(0x0001)) == 2.0 ** -24
 
 
+def test_fp16_round_matches_numpy_and_fixes_the_boundaries():
+    rng = np.random.default_rng(16)
+    # doubles across the whole binary16 range, subnormals and overflow included
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-30, 18, 200000))
+    assert np.array_equal(F.fp16_round(x), x.astype(np.float16).view(np.uint16))
+    # every binary16 value maps to itself; midpoints between neighbours go to the even one
+    bits = np.arange(0x7C00, dtype=np.uint16)
+    vals = F.fp16_decode(bits)
+    assert np.array_equal(F.fp16_round(vals), bits)
+    mid = (vals[:-1] + vals[1:]) / 2
+    want = np.where(bits[:-1] % 2 == 0, bits[:-1], bits[1:])
+    assert np.array_equal(F.fp16_round(mid), want)
+    # overflow: 65519.99 -> 65504, 65520 (the midpoint to 2^16) -> Inf; signs kept
+    assert F.fp16_round(65519.99) == 0x7BFF and F.fp16_round(65520.0) == 0x7C00
+    assert F.fp16_round(-1e9) == 0xFC00 and F.fp16_round(-0.0) == 0x8000
+    assert F.fp16_round(2.0 ** -25) == 0 and F.fp16_round(2.0 ** -25 * 1.0001) == 1
+
+
 def test_bf16_round_identity_and_midpoints():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = F.bf16_decode(bits)
