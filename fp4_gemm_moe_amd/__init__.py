@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQ_IN_FP16", "HQError",
+    "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQ_IN_FP16", "HQ_OUT_FP16", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
@@ -31,6 +31,7 @@ HQ_MXFP4 = 1
 HQ_NVFP4 = 2
 HQ_GS_INPUT = 1
 HQ_IN_FP16 = 2
+HQ_OUT_FP16 = 0x100      # OR'ed into a GEMM's mode: out is float16, not bfloat16
 HQ_SCALE_BROADCAST = 0
 HQ_SCALE_DIRECT = 1
 
@@ -164,12 +165,24 @@ def hq_group_wise_quant(mode, x, q, sf, global_scale=None, flags=0):
                                       _p(global_scale), flags))
 
 
+def _out_mode(mode, out):
+    """The mode passed to a GEMM call: HQ_OUT_FP16 added for a float16 out."""
+    return mode | (HQ_OUT_FP16 if out is not None and out.dtype == torch.float16 else 0)
+
+
+def _need_out(out, numel):
+    if out is not None and out.dtype == torch.float16:
+        _need(out, "out", torch.float16, numel)
+    else:
+        _need(out, "out", torch.bfloat16, numel)
+
+
 def _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, groups, bias_groups):
     _need(a, "a", torch.uint8, rows * code_cols(mode, k))
     _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
     _need(b, "b", torch.uint8, groups * n * code_cols(mode, k))
     _need(sfb, "sfb", torch.uint8, groups * n * (k // group_size(mode)))
-    _need(out, "out", torch.bfloat16, rows * n)
+    _need_out(out, rows * n)
     _need(bias, "bias", torch.bfloat16, bias_groups * n)
     _need(alpha, "alpha", torch.float32, bias_groups)
 
@@ -182,7 +195,7 @@ def hq_dense_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, m=None, n=No
     n = out.shape[-1] if n is None else n
     k = a.shape[-1] * (1 if mode == HQ_MXFP8 else 2) if k is None else k
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, m, n, k, 1, 1)
-    _check(load().hq_dense_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
+    _check(load().hq_dense_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
                                 _p(alpha), _p(out), m, n, k, cu_limit))
 
 
@@ -193,7 +206,7 @@ def hq_batch_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0):
     n = b.shape[1]
     k = kc * (1 if mode == HQ_MXFP8 else 2)
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, B * m, n, k, B, B)
-    _check(load().hq_batch_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
+    _check(load().hq_batch_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
                                 _p(alpha), _p(out), B, m, n, k, cu_limit))
 
 
@@ -206,7 +219,7 @@ def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, al
     k = kc * (1 if mode == HQ_MXFP8 else 2)
     _need(group_end, "group_end", torch.int32, E)
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, E, E)
-    _check(load().hq_group_contiguous_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
+    _check(load().hq_group_contiguous_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
                                            _p(group_end), E, _p(bias), _p(alpha), _p(out),
                                            rows, n, k, cu_limit))
 
@@ -232,13 +245,13 @@ def hq_group_contiguous_gemm_ptr_array(mode, a, sfa, bs, sfbs, group_end, out, n
     _need(a, "a", torch.uint8, rows * code_cols(mode, k))
     _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
     _need(group_end, "group_end", torch.int32, E)
-    _need(out, "out", torch.bfloat16, rows * n)
+    _need_out(out, rows * n)
     _need(bias, "bias", torch.bfloat16, E * n)
     _need(alpha, "alpha", torch.float32, E)
     dev = a.device
     bp = torch.tensor([t.data_ptr() for t in bs], dtype=torch.int64).to(dev, non_blocking=False)
     sp = torch.tensor([t.data_ptr() for t in sfbs], dtype=torch.int64).to(dev, non_blocking=False)
-    _check(load().hq_group_contiguous_gemm_ptr_array(_stream(a), mode, _p(a), _p(sfa), _p(bp), _p(sp),
+    _check(load().hq_group_contiguous_gemm_ptr_array(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(bp), _p(sp),
                                                      _p(group_end), E, _p(bias), _p(alpha), _p(out),
                                                      rows, n, k, cu_limit))
     return bp, sp     # keep the address arrays alive until the stream has run the call
@@ -280,7 +293,7 @@ def hq_group_masked_gemm(mode, a, sfa, b, sfb, masked_m, out, max_m, bias=None, 
         raise ValueError(f"a has {rows} rows, expected num_groups * max_m = {E * max_m}")
     _need(masked_m, "masked_m", torch.int32, E)
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, E, E)
-    _check(load().hq_group_masked_gemm(_stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb),
+    _check(load().hq_group_masked_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
                                        _p(masked_m), E, max_m, _p(bias), _p(alpha), _p(out),
                                        n, k, cu_limit))
 

@@ -113,7 +113,9 @@ __device__ inline int tile_group(const TileTable& t, int G, int gm) {
 
 // Four consecutive FP32 results of one output row -> BF16 (nearest even),
 // with the optional bias, written as one 8-byte store.
-__device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v, const uint16_t* bias4) {
+// Four FP32 results (+ BF16 bias) -> four BF16 (or, with f16, binary16)
+// values, each rounded to nearest even once.
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v, const uint16_t* bias4, bool f16 = false) {
   float f[4] = {v[0], v[1], v[2], v[3]};
   if (bias4 != nullptr) {
     uint2 bb = *reinterpret_cast<const uint2*>(bias4);
@@ -123,8 +125,14 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, v4f v, const uint16_
     f[3] += bf16_hi(bb.y);
   }
   uint2 o;
-  o.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
-  o.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  if (f16) {
+    auto h = [](float x) -> uint32_t { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); };
+    o.x = h(f[0]) | (h(f[1]) << 16);
+    o.y = h(f[2]) | (h(f[3]) << 16);
+  } else {
+    o.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
+    o.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
+  }
   *reinterpret_cast<uint2*>(dst) = o;
 }
 

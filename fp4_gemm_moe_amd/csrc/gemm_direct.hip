@@ -250,7 +250,7 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
           for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           const int64_t n = n0 + fn * 16 + 4 * q;
           if (m < tr.row_end && n < p.n)
-            store_bf16x4(p.out + m * p.n + n, v, bias ? bias + n : nullptr);
+            store_bf16x4(p.out + m * p.n + n, v, bias ? bias + n : nullptr, p.out_f16 != 0);
         }
       }
     }
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
           for (int i = 0; i < NW - 1; ++i) v += red[i][fm * FN + fn][lane];
           v = v * alpha;
           const int64_t n = n0 + fn * 16 + 4 * q;
-          if (m < tr.row_end && n < p.n) store_bf16x4(p.out + m * p.n + n, v, nullptr);
+          if (m < tr.row_end && n < p.n) store_bf16x4(p.out + m * p.n + n, v, nullptr, p.out_f16 != 0);
         }
       }
     }

@@ -436,6 +436,14 @@ __device__ __forceinline__ void bar() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Two FP32 values -> packed binary16 pair (low half = a), round to nearest
+// even (Inf beyond the largest finite value).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+}
+
 // Two FP32 values -> packed BF16 pair (low half = a), round to nearest even,
 // in one hardware conversion.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -445,11 +453,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Epilogues (separate instantiations, so that one costs the others no
-// registers): kEpiBf16 writes the BF16 output; kEpiSplit (the launch has a
+// registers): kEpiBf16 writes the BF16 output (kEpiF16: binary16, for
+// p.out_f16); kEpiSplit (the launch has a
 // K split, p.ksplit > 1) writes FP32 partial tiles; kEpiSwiglu (MXFP8, p.h > 0,
 // PAIRED B rows) applies SwiGLU and the MXFP8 re-quant and writes codes and
 // scales of y instead of the gate|up output.
-constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2;
+constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3;
 
 template <int FMT, int EPI, bool GS>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
@@ -915,6 +924,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
       const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
       const float alpha = FMT == kNV ? p.alpha[tl.g] : 1.0f;   // NVFP4: g_A * g_B per group
+      constexpr bool F16O = EPI == kEpiF16;                    // binary16 instead of BF16
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
         v4f bq[4];
@@ -937,8 +947,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               f[r] = FMT == kNV ? acc[i][j][4 * b + r] * alpha : acc[i][j][4 * b + r] + bq[b][r];
-            pk[b][0] = pack_bf16x2(f[0], f[1]);
-            pk[b][1] = pack_bf16x2(f[2], f[3]);
+            pk[b][0] = F16O ? pack_f16x2(f[0], f[1]) : pack_bf16x2(f[0], f[1]);
+            pk[b][1] = F16O ? pack_f16x2(f[2], f[3]) : pack_bf16x2(f[2], f[3]);
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) {            // e = 0: quads b = 0/1, e = 1: b = 2/3
@@ -1013,7 +1023,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
         for (int r = 0; r < 4; ++r) f[r] = v[r];
       }
       *reinterpret_cast<uint2*>(p.out + row * ldo + 4 * c) =
-          make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+          p.out_f16 ? make_uint2(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]))
+                    : make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
     }
   }
 }
@@ -1055,6 +1066,9 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiBf16, GS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiF16, GS>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiSplit, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               smem);
@@ -1114,8 +1128,12 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
         q1.ksplit = 1;
         q1.partial = nullptr;
         q1.tile_limit = (int32_t)(tiles - cols * mb);
-        hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS), smem,
-                           s, q1);
+        if (q1.out_f16)
+          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
+                             smem, s, q1);
+        else
+          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
+                             smem, s, q1);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess) {
           int64_t g2 = cols * mb * S;
@@ -1163,6 +1181,8 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (grid < 1) grid = 1;
   if (q.ksplit > 1)
     hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+  else if (q.out_f16)
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   else
     hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   hipError_t e = hipGetLastError();

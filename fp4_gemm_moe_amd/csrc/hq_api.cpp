@@ -168,6 +168,8 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
                         const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
                         const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
                         int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
   GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, 1, "hq_dense_gemm"};
   bool noop;
   hq_status st = check_gemm(c, &noop);
@@ -176,6 +178,7 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
   p.form = hq::kUniform;
   p.num_groups = 1;
   p.m_rows = m;
@@ -187,6 +190,8 @@ hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
                         const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
                         const float* alpha, uint16_t* out, int64_t batch, int64_t m, int64_t n,
                         int64_t k, int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
   const char* what = "hq_batch_gemm";
   if (batch < 0 || batch > kI32) return fail(HQ_ERR_SHAPE, "%s: batch=%lld out of range", what, (long long)batch);
   if (m < 0 || (batch > 0 && m > kI32 / (batch > 0 ? batch : 1)))
@@ -199,6 +204,7 @@ hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
   p.form = hq::kUniform;
   p.num_groups = (int32_t)batch;
   p.m_rows = batch * m;
@@ -211,6 +217,8 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
                                    const int32_t* group_end, int32_t num_groups,
                                    const uint16_t* bias, const float* alpha, uint16_t* out,
                                    int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
   const char* what = "hq_group_contiguous_gemm";
   if (num_groups < 1 || num_groups > 1024)
     return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
@@ -223,6 +231,7 @@ hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
   p.form = hq::kContiguous;
   p.group_end = group_end;
   p.num_groups = num_groups;
@@ -237,6 +246,8 @@ hq_status hq_group_contiguous_gemm_ptr_array(void* stream, int32_t mode, const u
                                              int32_t num_groups, const uint16_t* bias,
                                              const float* alpha, uint16_t* out, int64_t m_total,
                                              int64_t n, int64_t k, int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
   const char* what = "hq_group_contiguous_gemm_ptr_array";
   if (num_groups < 1 || num_groups > 1024)
     return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
@@ -251,6 +262,7 @@ hq_status hq_group_contiguous_gemm_ptr_array(void* stream, int32_t mode, const u
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   hq::GemmArgs p = make_args(mode, a, sfa, nullptr, nullptr, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
   p.form = hq::kContiguous;
   p.group_end = group_end;
   p.num_groups = num_groups;
@@ -306,6 +318,8 @@ hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, con
                                int32_t num_groups, int64_t max_m_per_group, const uint16_t* bias,
                                const float* alpha, uint16_t* out, int64_t n, int64_t k,
                                int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
   const char* what = "hq_group_masked_gemm";
   if (num_groups < 1 || num_groups > 1024)
     return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
@@ -321,6 +335,7 @@ hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, con
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
   p.form = hq::kMasked;
   p.counts = masked_m;
   p.num_groups = num_groups;

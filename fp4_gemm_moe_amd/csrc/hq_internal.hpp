@@ -63,6 +63,7 @@ struct GemmArgs {
   // and the strides are then unused.  nullptr: one [groups, n, K'] tensor.
   const uint64_t* b_ptrs;
   const uint64_t* sfb_ptrs;
+  int32_t out_f16;      // out holds IEEE binary16 instead of BF16 (round to nearest even)
 };
 
 struct DeviceInfo {

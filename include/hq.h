@@ -69,6 +69,13 @@ typedef int32_t hq_status;
 #define HQ_ERR_DEVICE (-5) /* current device is not gfx950 / HIP error      */
 #define HQ_ERR_LAUNCH (-6) /* a kernel launch failed                        */
 
+/* OR'ed into the mode of hq_dense_gemm, hq_batch_gemm, hq_group_contiguous_gemm,
+ * hq_group_contiguous_gemm_ptr_array and hq_group_masked_gemm: out holds IEEE
+ * binary16 (FP16) values, each rounded to nearest even from the FP32 result
+ * (+ bias, x alpha; Inf beyond 65504), instead of BF16 (the flashrt/fp4-gemm
+ * page's *_fp16 GEMMs).  bias stays BF16. */
+#define HQ_OUT_FP16 0x100
+
 /* hq_group_wise_quant flags */
 #define HQ_GS_INPUT 1u /* NVFP4: read the global scale from *global_scale   */
 #define HQ_IN_FP16 2u  /* x holds IEEE binary16 (FP16) patterns, not BF16  */
