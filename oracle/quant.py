@@ -101,10 +101,14 @@ def nvfp4_quant_values(x, g=None):
     d = np.float32(np.float32(6.0) * g)
     blk = x32.reshape(x32.shape[:-1] + (K // NV_GROUP, NV_GROUP))
     amax_b = np.max(np.abs(blk), axis=-1).astype(np.float32)
-    ratio = (amax_b / d).astype(np.float32)                    # one fp32 division
+    # A quotient may overflow FP32 (a tiny supplied g): it becomes +-Inf and
+    # the encoders saturate it, as the device does; the warning is silenced.
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        ratio = (amax_b / d).astype(np.float32)                # one fp32 division
     sf = F.ue4m3_encode(ratio.astype(np.float64))
-    s_eff = (F.ue4m3_decode(sf).astype(np.float32) * g).astype(np.float32)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(over="ignore"):
+        s_eff = (F.ue4m3_decode(sf).astype(np.float32) * g).astype(np.float32)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
         q = (blk / s_eff[..., None]).astype(np.float32)        # one fp32 division
     q = np.where(s_eff[..., None] == 0, np.copysign(np.float32(0), blk), q)
     codes = F.e2m1_encode(q.astype(np.float64)).reshape(x.shape)
