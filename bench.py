@@ -11,14 +11,30 @@ Default workload (one "step" = one pass of the MoE expert forward hot path):
        BF16 [R, 3072], then hq_fused_swiglu_quant; the per-kernel pass also
        times these two calls beside the fused one)
   Weights are quantised once before timing (they are static parameters).
+  The timed loop records HIP events around every launch on the stream the
+  kernels run on, so the per-kernel times (and the roofline of the dominant
+  kernel) come from the timed steps themselves.
+
+After the headline the default run times one launch configuration of each
+other workload ("configs" in the JSON line; --no-configs skips them, --only
+ID runs one of them alone, e.g. under a profiler):
+  d0  dense MXFP8 256^3 (seed 0)
+  d1  batch MXFP8 4 x 256^3 with and without bias; dense MXFP4 32 x 512 x 256
+  d2  dense MXFP4 / NVFP4, N = 17408, K = 5120, M in {1, 512, 4096} (caller
+      workspace: K split at M = 512, tail split at 4096)
+  d4  grouped-masked MXFP4, 64 experts x 256-row slots, K = 7168, N = 4096
+  d5  quantisation bandwidth: MXFP4 [16384, 7168], NVFP4 [4096, 17408] (global
+      scale supplied, and with the amax pass)
+each with its time, achieved rate, roofline fraction and, where affordable,
+the oracle's time for the same work on the host cores.
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
 of the valid rows per second), the per-kernel times, the roofline of the
-dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak)
-and the oracle timed on a bounded sample on the host cores.
+dominant kernel (the grouped GEMM, against the dense MXFP8 matrix-core peak),
+the oracle timed on a bounded sample on the host cores, and the configs.
 
-    python bench.py [--steps K] [--warmup W]
-                    [--workload moe|moe_unfused|moe_mlp|dense_fp4|masked_fp4|permute]
+    python bench.py [--steps K] [--warmup W] [--no-configs] [--only ID]
+                    [--workload moe|moe_unfused|moe_mlp|dense_fp4|masked_fp4|permute|configs]
     python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
                                         # one JSON line per case
 """
@@ -48,22 +64,31 @@ def _dev_bf16(torch, bits, dev):
 
 
 class Timer:
-    """Per-kernel HIP-event timing on the stream the kernels run on."""
+    """Per-kernel HIP-event timing on the stream the kernels run on (the
+    binding launches on torch.cuda.current_stream(), where the events are
+    recorded)."""
 
     def __init__(self, torch):
         self.torch = torch
         self.ev = {}
 
     def mark(self, name, fn):
+        stream = self.torch.cuda.current_stream()
         s = self.torch.cuda.Event(enable_timing=True)
         e = self.torch.cuda.Event(enable_timing=True)
-        s.record()
+        s.record(stream)
         fn()
-        e.record()
+        e.record(stream)
         self.ev.setdefault(name, []).append((s, e))
 
+    def times_ms(self, name):
+        return [s.elapsed_time(e) for s, e in self.ev[name]]
+
     def mean_ms(self, name):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.ev[name]]))
+        return float(np.mean(self.times_ms(name)))
+
+    def median_ms(self, name):
+        return float(np.median(self.times_ms(name)))
 
 
 def _traffic(kernel_key):
@@ -123,7 +148,9 @@ def run_moe(args, torch, hq, synth, down=False, fused=False):
 
     timer = Timer(torch)
 
-    def step(t=None):
+    def step(t=None, timed=True):
+        """One step; with a timer, events around each launch.  timed=False:
+        the two-call form of the fused step, timed beside it."""
         f1 = lambda: hq.hq_group_wise_quant("mxfp8", x, aq, asf)
         f2 = lambda: hq.hq_group_contiguous_gemm("mxfp8", aq, asf, wq, wsf, ge, out)
         f3 = lambda: hq.hq_fused_swiglu_quant("mxfp8", out, yq, ysf, E, ge, 0, valid)
@@ -137,12 +164,16 @@ def run_moe(args, torch, hq, synth, down=False, fused=False):
                 f1(); f2(); f3()
             if down:
                 f4()
+        elif not timed:
+            t.mark("gemm", f2)
+            t.mark("swiglu", f3)
         else:
             t.mark("quant", f1)
             if fused:
                 t.mark("gemm_swiglu", f5)
-            t.mark("gemm", f2)           # the two-call form, reported beside the fused one
-            t.mark("swiglu", f3)
+            else:
+                t.mark("gemm", f2)
+                t.mark("swiglu", f3)
             if down:
                 t.mark("down", f4)
 
@@ -151,17 +182,26 @@ def run_moe(args, torch, hq, synth, down=False, fused=False):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    # the timed steps: events around every launch, and around the whole run
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_start.record(stream)
     for _ in range(args.steps):
-        step()
+        step(timer, timed=True)
+    t_stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # separate pass with per-kernel events (same launches, same stream)
-    for _ in range(args.steps):
-        step(timer)
-    torch.cuda.synchronize()
+    # the two-call form beside the fused one (not part of the step)
+    if fused:
+        for _ in range(args.steps):
+            step(timer, timed=False)
+        torch.cuda.synchronize()
 
-    ms_step = wall * 1e3 / args.steps
+    ms_step = t_start.elapsed_time(t_stop) / args.steps
+    log(f"step {ms_step:.4f} ms (events), {wall * 1e3 / args.steps:.4f} ms (host clock)")
     flops = 2.0 * T * N * K
     quant_bytes = R * K * (2 + 1 + 1 / 32)     # the whole padded activation buffer
     swiglu_bytes = T * H * (4 + 1 + 1 / 32)
@@ -185,6 +225,8 @@ def run_moe(args, torch, hq, synth, down=False, fused=False):
     if fused:
         kernels["grouped_gemm_mxfp8"]["note"] = "two-call form, timed beside the step"
         kernels["swiglu_quant_mxfp8"]["note"] = "two-call form, timed beside the step"
+    for v in kernels.values():
+        v["launches"] = args.steps
     gkey = gkeys[0][1]                  # the step's GEMM: the roofline's kernel
     gemm_ms = kernels[gkey]["ms"]
     gemm_tflops = kernels[gkey]["TFLOP/s"]
@@ -201,7 +243,8 @@ def run_moe(args, torch, hq, synth, down=False, fused=False):
     roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_TFLOPS["mxfp8"],
             "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_TFLOPS["mxfp8"],
             "traffic": _traffic(gkey),
-            "kernel": gkey, "flop_per_launch": flops}
+            "kernel": gkey, "flop_per_launch": flops, "mean_launch_ms": gemm_ms,
+            "median_launch_ms": timer.median_ms(gkeys[0][0]), "launches": args.steps}
     step_flops = flops + (down_flops if down else 0.0)
     value = step_flops / (ms_step * 1e-3) / 1e12
     ctx = None if down else {"counts": counts, "ends": ends, "a": d["a"], "b": d["b"], "K": K, "N": N, "H": H}
@@ -296,7 +339,8 @@ def run_dense_fp4(args, torch, hq, synth):
     alpha = (ga * gw) if mode == "nvfp4" else None
     out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
     timer = Timer(torch)
-    f = lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha)
+    ws = hq.gemm_workspace(mode, m, n, k, device=dev)
+    f = lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha, workspace=ws)
     for _ in range(args.warmup):
         f()
     torch.cuda.synchronize()
@@ -399,11 +443,13 @@ def run_sweep(args, torch, hq, synth):
                 aq, asf, ga = hq.quantize(x, mode)
                 alpha = (ga * gw) if mode == "nvfp4" else None
                 out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-                warm = _time_us(torch, [lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha)])
+                ws = hq.gemm_workspace(mode, m, n, k, device=dev)
+                warm = _time_us(torch, [lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha,
+                                                                 workspace=ws)])
                 cold = None
                 if m <= 16:
                     cold = _time_us(torch, [lambda q=q, s_=s_: hq.hq_dense_gemm(mode, aq, asf, q, s_, out,
-                                                                                   alpha=alpha)
+                                                                                   alpha=alpha, workspace=ws)
                                             for q, s_ in ring])
                 flops = 2.0 * m * n * k
                 gs = 16 if mode == "nvfp4" else 32
@@ -452,19 +498,257 @@ def run_sweep(args, torch, hq, synth):
         torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------- per-config records
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _launch_us(torch, fns, reps=30, warm=5):
+    """Per-launch times (HIP events around each launch on the current stream)
+    over `reps` launches after `warm` untimed ones; fns is cycled (a ring of
+    buffers for cold-cache timing).  Returns (median us, mean us)."""
+    for i in range(warm):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for i in range(reps):
+        t.mark("x", fns[(warm + i) % len(fns)])
+    torch.cuda.synchronize()
+    v = np.array(t.times_ms("x")) * 1e3
+    return float(np.median(v)), float(np.mean(v))
+
+
+def _oracle_us(fn, reps=3):
+    best = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        best.append(time.perf_counter() - t0)
+    return float(np.median(best)) * 1e6
+
+
+def _rec(cid, workload, us, flops=None, bytes_=None, bound="mfma", peak_key="mxfp8", **extra):
+    """One config record: time, achieved rate against the bound's peak."""
+    r = {"id": cid, "workload": workload, "us": round(us, 2)}
+    if flops is not None:
+        r["TFLOP/s"] = round(flops / (us * 1e-6) / 1e12, 2)
+    if bytes_ is not None:
+        r["GB/s"] = round(bytes_ / (us * 1e-6) / 1e9, 1)
+    if bound == "hbm":
+        r.update(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", frac=round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3))
+    else:
+        pk = PEAK_TFLOPS[peak_key]
+        r.update(bound=bound, peak=pk, unit="TFLOP/s", frac=round(flops / (us * 1e-6) / 1e12 / pk, 4))
+    r.update(extra)
+    return r
+
+
+CONFIG_IDS = ["d0", "d1_batch", "d1_batch_bias", "d1_mxfp4",
+              "d2_mxfp4_M1", "d2_mxfp4_M512", "d2_mxfp4_M4096",
+              "d2_nvfp4_M1", "d2_nvfp4_M512", "d2_nvfp4_M4096",
+              "d4", "d5_mxfp4", "d5_nvfp4", "d5_nvfp4_amax"]
+
+
+def run_configs(torch, hq, synth, only=None, oracle=True):
+    """One record per config (see the module docstring).  `only`: a config id
+    (or a prefix, e.g. "d2") to run alone."""
+    from oracle import gemm as G
+    from oracle import quant as Q
+    dev = torch.device("cuda:0")
+    want = lambda cid: only is None or cid.startswith(only)
+    recs = []
+    threads = _oracle_threads()
+
+    def emit(r):
+        log(f"config {r['id']}: {r['us']} us, frac {r['frac']}")
+        recs.append(r)
+
+    # d0: dense MXFP8 256^3, seed 0
+    if want("d0"):
+        d = synth.dense_mxfp8_256()
+        qa, sa, _ = hq.quantize(_dev_bf16(torch, d["a"], dev), "mxfp8")
+        qb, sb, _ = hq.quantize(_dev_bf16(torch, d["b"], dev), "mxfp8")
+        out = torch.empty(256, 256, dtype=torch.bfloat16, device=dev)
+        med, mean = _launch_us(torch, [lambda: hq.hq_dense_gemm("mxfp8", qa, sa, qb, sb, out)])
+        extra = {"mean_us": round(mean, 2)}
+        if oracle:
+            a, sfa = Q.mx_quant_bf16(d["a"], "mxfp8")
+            b, sfb = Q.mx_quant_bf16(d["b"], "mxfp8")
+            extra.update(oracle_us=round(_oracle_us(lambda: G.dense_gemm("mxfp8", a, sfa, b, sfb)), 1),
+                         oracle_cores=threads)
+        emit(_rec("d0", "dense_mxfp8_M256_N256_K256", med, flops=2.0 * 256 ** 3, bound="latency", **extra))
+
+    # d1: batch MXFP8 4 x 256^3 (with and without bias), dense MXFP4 32 x 512 x 256
+    if want("d1_batch") or want("d1_batch_bias"):
+        d = synth.batch_mxfp8()
+        Bn, m, n, k = 4, 256, 256, 256
+        qa, sa, _ = hq.quantize(_dev_bf16(torch, d["a"].reshape(Bn * m, k), dev), "mxfp8")
+        qb, sb, _ = hq.quantize(_dev_bf16(torch, d["b"].reshape(Bn * n, k), dev), "mxfp8")
+        bias = _dev_bf16(torch, d["bias"], dev)
+        out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
+        args = (qa.view(Bn, m, k), sa.view(Bn, m, -1), qb.view(Bn, n, k), sb.view(Bn, n, -1), out)
+        for cid, bb in (("d1_batch", None), ("d1_batch_bias", bias)):
+            if not want(cid):
+                continue
+            med, mean = _launch_us(torch, [lambda bb=bb: hq.hq_batch_gemm("mxfp8", *args, bias=bb)])
+            extra = {"mean_us": round(mean, 2)}
+            if oracle:
+                a, sfa = Q.mx_quant_bf16(d["a"].reshape(Bn * m, k), "mxfp8")
+                b, sfb = Q.mx_quant_bf16(d["b"].reshape(Bn * n, k), "mxfp8")
+                ob = None if bb is None else d["bias"]
+                extra.update(oracle_us=round(_oracle_us(lambda: G.batch_gemm(
+                    "mxfp8", a.reshape(Bn, m, k), sfa.reshape(Bn, m, -1), b.reshape(Bn, n, k),
+                    sfb.reshape(Bn, n, -1), bias=ob)), 1), oracle_cores=threads)
+            emit(_rec(cid, "batch_mxfp8_B4_M256_N256_K256" + ("_bias" if bb is not None else ""), med,
+                      flops=2.0 * Bn * m * n * k, bound="latency", **extra))
+    if want("d1_mxfp4"):
+        d = synth.dense_mxfp4_small()
+        qa, sa, _ = hq.quantize(_dev_bf16(torch, d["a"], dev), "mxfp4")
+        qb, sb, _ = hq.quantize(_dev_bf16(torch, d["b"], dev), "mxfp4")
+        out = torch.empty(32, 512, dtype=torch.bfloat16, device=dev)
+        med, mean = _launch_us(torch, [lambda: hq.hq_dense_gemm("mxfp4", qa, sa, qb, sb, out)])
+        extra = {"mean_us": round(mean, 2)}
+        if oracle:
+            a, sfa = Q.mx_quant_bf16(d["a"], "mxfp4")
+            b, sfb = Q.mx_quant_bf16(d["b"], "mxfp4")
+            extra.update(oracle_us=round(_oracle_us(lambda: G.dense_gemm("mxfp4", a, sfa, b, sfb)), 1),
+                         oracle_cores=threads)
+        emit(_rec("d1_mxfp4", "dense_mxfp4_M32_N512_K256", med, flops=2.0 * 32 * 512 * 256, bound="latency",
+                  peak_key="mxfp4", **extra))
+
+    # d2: dense FP4 cells at (N, K) = (17408, 5120)
+    n, k = 17408, 5120
+    if any(want(f"d2_{md}_M{m}") for md in ("mxfp4", "nvfp4") for m in (1, 512, 4096)):
+        wbits = synth.dense_fp4_large_weights(n, k)
+        w = _dev_bf16(torch, wbits, dev)
+        for mode in ("mxfp4", "nvfp4"):
+            if not any(want(f"d2_{mode}_M{m}") for m in (1, 512, 4096)):
+                continue
+            wq, wsf, gw = hq.quantize(w, mode)
+            gs = 16 if mode == "nvfp4" else 32
+            for m in (1, 512, 4096):
+                cid = f"d2_{mode}_M{m}"
+                if not want(cid):
+                    continue
+                abits = synth.dense_fp4_large_acts(n, k, m)
+                aq, asf, ga = hq.quantize(_dev_bf16(torch, abits, dev), mode)
+                alpha = (ga * gw) if mode == "nvfp4" else None
+                out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+                ws = hq.gemm_workspace(mode, m, n, k, device=dev)
+                flops = 2.0 * m * n * k
+                bytes_ = (m + n) * k * (0.5 + 1 / gs) + 2 * m * n
+                if m == 1:
+                    # weights rotated through a ring of >= 1 GB (larger than the 256 MB MALL)
+                    copies = max(1, -(-(1 << 30) // (wq.numel() + wsf.numel())))
+                    ring = [(wq, wsf)] + [(wq.clone(), wsf.clone()) for _ in range(copies - 1)]
+                    fns = [lambda q=q, s_=s_: hq.hq_dense_gemm(mode, aq, asf, q, s_, out, alpha=alpha, workspace=ws)
+                           for q, s_ in ring]
+                else:
+                    fns = [lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha, workspace=ws)]
+                med, mean = _launch_us(torch, fns, reps=30 if m < 4096 else 20)
+                extra = {"mean_us": round(mean, 2), "workspace_bytes": 0 if ws is None else ws.numel()}
+                if oracle and m == 1:
+                    if mode == "nvfp4":
+                        ca, sa_, g_a = Q.nvfp4_quant_bf16(abits)
+                        cb, sb_, g_b = Q.nvfp4_quant_bf16(wbits)
+                        al = np.float32(np.float32(g_a) * np.float32(g_b))
+                    else:
+                        (ca, sa_), (cb, sb_), al = Q.mx_quant_bf16(abits, mode), Q.mx_quant_bf16(wbits, mode), None
+                    extra.update(oracle_us=round(_oracle_us(lambda: G.dense_gemm(mode, ca, sa_, cb, sb_, alpha=al),
+                                                            reps=1), 1), oracle_cores=threads)
+                if m == 1:
+                    emit(_rec(cid, f"dense_{mode}_M{m}_N{n}_K{k}_cold", med, flops=flops, bytes_=bytes_,
+                              bound="hbm", **extra))
+                else:
+                    emit(_rec(cid, f"dense_{mode}_M{m}_N{n}_K{k}", med, flops=flops, bytes_=bytes_, bound="mfma",
+                              peak_key="nvfp4_f16" if mode == "nvfp4" else "mxfp4", **extra))
+                del aq, asf, out, ws
+                if m == 1:
+                    del ring, fns
+            del wq, wsf
+        del w
+        torch.cuda.empty_cache()
+
+    # d4: grouped-masked MXFP4 (64 experts, 256-row slots, K = 7168, N = 4096)
+    if want("d4"):
+        d = synth.moe_masked(threads=16)
+        E, Mmax, K, N = 64, d["max_m"], d["K"], d["N"]
+        counts = d["counts"]
+        T = int(counts.sum())
+        aq, asf, _ = hq.quantize(_dev_bf16(torch, d["a"], dev), "mxfp4")
+        w = _dev_bf16(torch, d["b"].reshape(E * N, K), dev)
+        wq, wsf, _ = hq.quantize(w, "mxfp4")
+        del w
+        wq, wsf = wq.view(E, N, K // 2), wsf.view(E, N, K // 32)
+        cnt = torch.from_numpy(counts.astype(np.int32)).to(dev)
+        out = torch.empty(E * Mmax, N, dtype=torch.bfloat16, device=dev)
+        med, mean = _launch_us(torch, [lambda: hq.hq_group_masked_gemm("mxfp4", aq, asf, wq, wsf, cnt, out, Mmax)],
+                               reps=20)
+        experts = int((counts > 0).sum())
+        bytes_ = T * K * (0.5 + 1 / 32) + experts * N * K * (0.5 + 1 / 32) + 2 * T * N
+        emit(_rec("d4", "moe_grouped_masked_mxfp4_E64_Mmax256_K7168_N4096", med, flops=2.0 * T * N * K,
+                  bytes_=bytes_, bound="hbm", mean_us=round(mean, 2), routed_rows=T,
+                  mfma_frac=round(2.0 * T * N * K / (med * 1e-6) / 1e12 / PEAK_TFLOPS["mxfp4"], 4)))
+        del aq, asf, wq, wsf, out, d
+        torch.cuda.empty_cache()
+
+    # d5: quantisation bandwidth (input ring of >= 1 GB: past the MALL)
+    rng = np.random.default_rng(5)
+    for cid, mode, m, kk, supplied in (("d5_mxfp4", "mxfp4", 16384, 7168, False),
+                                       ("d5_nvfp4", "nvfp4", 4096, 17408, True),
+                                       ("d5_nvfp4_amax", "nvfp4", 4096, 17408, False)):
+        if not want(cid):
+            continue
+        xbits = synth.normal_bf16(rng, (m, kk))
+        x = _dev_bf16(torch, xbits, dev)
+        xs = [x] + [x.clone() for _ in range(max(1, -(-(1 << 30) // (2 * m * kk))) - 1)]
+        q, sf, g = hq.quantize(x, mode)
+        gin = g.clone() if supplied else None
+        if gin is None:
+            fns = [lambda xx=xx: hq.hq_group_wise_quant(mode, xx, q, sf, g) for xx in xs]
+        else:
+            fns = [lambda xx=xx: hq.hq_group_wise_quant(mode, xx, q, sf, gin, hq.HQ_GS_INPUT) for xx in xs]
+        med, mean = _launch_us(torch, fns, reps=30)
+        gs = 16 if mode == "nvfp4" else 32
+        bytes_ = m * kk * (2 + 0.5 + 1 / gs)
+        extra = {"mean_us": round(mean, 2)}
+        if mode == "nvfp4" and not supplied:
+            extra["GB/s_incl_amax_pass"] = round((bytes_ + 2 * m * kk) / (med * 1e-6) / 1e9, 1)
+        if oracle:
+            rows = 256
+            sample = xbits[:rows]
+            fn = (lambda: Q.mx_quant_bf16(sample, mode)) if mode != "nvfp4" else (
+                lambda: Q.nvfp4_quant_bf16(sample, None if not supplied else np.float32(g.item())))
+            ous = _oracle_us(fn)
+            extra.update(oracle_GB_s=round(rows * kk * (2 + 0.5 + 1 / gs) / (ous * 1e-6) / 1e9, 3),
+                         oracle_sample=f"{rows} rows", oracle_cores=threads)
+        emit(_rec(cid, f"quant_{mode}_{m}x{kk}" + ("_g_supplied" if supplied else ("_amax" if mode == "nvfp4"
+                                                                                   else "")) + "_cold",
+                  med, bytes_=bytes_, bound="hbm", **extra))
+        del x, xs, q, sf
+        torch.cuda.empty_cache()
+    return recs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe", choices=["moe", "moe_unfused", "moe_mlp", "dense_fp4",
-                                                       "masked_fp4", "permute", "sweep"])
+                                                       "masked_fp4", "permute", "sweep", "configs"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
     ap.add_argument("--k", type=int, default=5120)
     ap.add_argument("--tokens", type=int, default=1024, help="--workload permute: token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config records")
+    ap.add_argument("--only", default=None, help="run one config record alone (--workload configs)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -496,6 +780,11 @@ def main():
     if args.workload == "sweep":
         run_sweep(args, torch, hq, synth)
         return
+    if args.workload == "configs":
+        recs = run_configs(torch, hq, synth, only=args.only, oracle=not args.no_cpu_baseline)
+        print(json.dumps({"configs": recs, "device": {"name": props.name,
+                                                       "cus": props.multi_processor_count}}), flush=True)
+        return
     runner = {"moe": lambda *a: run_moe(*a, fused=True), "moe_unfused": run_moe,
               "dense_fp4": run_dense_fp4, "masked_fp4": run_masked_fp4, "permute": run_permute,
               "moe_mlp": lambda *a: run_moe(*a, down=True, fused=True)}[args.workload]
@@ -506,6 +795,11 @@ def main():
     if ctx is not None and not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         cpu = cpu_baseline_moe(ctx)
+    recs = None
+    if args.workload == "moe" and not args.no_configs:
+        del ctx
+        torch.cuda.empty_cache()
+        recs = run_configs(torch, hq, synth, oracle=not args.no_cpu_baseline)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -524,6 +818,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "configs": recs,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)

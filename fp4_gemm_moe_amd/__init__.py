@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQ_IN_FP16", "HQ_OUT_FP16", "HQError",
-    "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
+    "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm", "hq_gemm_workspace_size",
+    "gemm_workspace", "ptr_arrays",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
@@ -40,6 +41,7 @@ MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
 
 EXPORTED_SYMBOLS = (
     "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
+    "hq_dense_gemm_ws", "hq_batch_gemm_ws", "hq_gemm_workspace_size",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm",
@@ -63,12 +65,18 @@ _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _U32 = ctypes.c_uint32
+_U64 = ctypes.c_uint64
 
 _SIGS = {
     "hq_last_error": ([], ctypes.c_char_p),
     "hq_group_wise_quant": ([_VP, _I32, _VP, _I64, _I64, _VP, _VP, _VP, _U32], _I32),
     "hq_dense_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_batch_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32], _I32),
+    "hq_dense_gemm_ws": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _VP, _U64],
+                         _I32),
+    "hq_batch_gemm_ws": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32, _VP,
+                          _U64], _I32),
+    "hq_gemm_workspace_size": ([_I32, _I64, _I64, _I64, _I64, _I32, ctypes.POINTER(ctypes.c_uint64)], _I32),
     "hq_group_contiguous_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                   _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm_ptr_array": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
@@ -155,6 +163,7 @@ def hq_group_wise_quant(mode, x, q, sf, global_scale=None, flags=0):
     mode = _mode(mode)
     m, k = x.shape
     if x.dtype == torch.float16:
+        _need(x, "x", torch.float16)
         flags |= HQ_IN_FP16
     else:
         _need(x, "x", torch.bfloat16)
@@ -187,27 +196,59 @@ def _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, rows, n, k, groups, bia
     _need(alpha, "alpha", torch.float32, bias_groups)
 
 
+def _workspace(ws):
+    """(pointer, bytes) of a caller workspace tensor (any dtype, contiguous,
+    on the device), or (None, 0)."""
+    if ws is None:
+        return None, 0
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return _p(ws), ws.numel() * ws.element_size()
+
+
+def hq_gemm_workspace_size(mode, m, n, k, batch=1, cu_limit=0):
+    """Bytes of FP32 workspace a dense (batch=1) or batch GEMM of this shape
+    uses on the current device (0: it never splits K)."""
+    out = ctypes.c_uint64(0)
+    _check(load().hq_gemm_workspace_size(_mode(mode), batch, m, n, k, cu_limit, ctypes.byref(out)))
+    return int(out.value)
+
+
+def gemm_workspace(mode, m, n, k, batch=1, cu_limit=0, device=None):
+    """Allocates (with torch) the workspace hq_gemm_workspace_size asks for:
+    a uint8 device tensor, or None when the shape needs none.  Allocate it
+    before graph capture and pass it on every call."""
+    nbytes = hq_gemm_workspace_size(mode, m, n, k, batch, cu_limit)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
 def hq_dense_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, m=None, n=None, k=None,
-                  cu_limit=0):
-    """out[m, n] = a[m, k] * b[n, k]^T (+bias[n]) (*alpha[0]) in BF16."""
+                  cu_limit=0, workspace=None):
+    """out[m, n] = a[m, k] * b[n, k]^T (+bias[n]) (*alpha[0]) in BF16.  With a
+    workspace tensor (gemm_workspace) the call may split K (hq_dense_gemm_ws)."""
     mode = _mode(mode)
     m = out.shape[0] if m is None else m
     n = out.shape[-1] if n is None else n
     k = a.shape[-1] * (1 if mode == HQ_MXFP8 else 2) if k is None else k
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, m, n, k, 1, 1)
-    _check(load().hq_dense_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
-                                _p(alpha), _p(out), m, n, k, cu_limit))
+    wp, wb = _workspace(workspace)
+    _check(load().hq_dense_gemm_ws(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
+                                   _p(bias), _p(alpha), _p(out), m, n, k, cu_limit, wp, wb))
 
 
-def hq_batch_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0):
-    """out[B, m, n] = a[B, m, k] * b[B, n, k]^T per batch item."""
+def hq_batch_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0, workspace=None):
+    """out[B, m, n] = a[B, m, k] * b[B, n, k]^T per batch item (a workspace:
+    hq_batch_gemm_ws)."""
     mode = _mode(mode)
     B, m, kc = a.shape
     n = b.shape[1]
     k = kc * (1 if mode == HQ_MXFP8 else 2)
     _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, B * m, n, k, B, B)
-    _check(load().hq_batch_gemm(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb), _p(bias),
-                                _p(alpha), _p(out), B, m, n, k, cu_limit))
+    wp, wb = _workspace(workspace)
+    _check(load().hq_batch_gemm_ws(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
+                                   _p(bias), _p(alpha), _p(out), B, m, n, k, cu_limit, wp, wb))
 
 
 def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, alpha=None,
@@ -224,33 +265,51 @@ def hq_group_contiguous_gemm(mode, a, sfa, b, sfb, group_end, out, bias=None, al
                                            rows, n, k, cu_limit))
 
 
-def hq_group_contiguous_gemm_ptr_array(mode, a, sfa, bs, sfbs, group_end, out, n, bias=None,
-                                       alpha=None, cu_limit=0):
-    """Grouped-contiguous GEMM whose group g uses the separate weight tensors
-    bs[g] [n, K'] and sfbs[g] [n, k/gs] (uint8, contiguous, 16-byte aligned):
-    the binding builds the device arrays of their addresses."""
+def ptr_arrays(mode, bs, sfbs, n, k):
+    """Device arrays (int64) of the addresses of per-expert weight tensors
+    bs[g] [n, K'] and sfbs[g] [n, k/gs] (uint8, contiguous, 16-byte aligned),
+    checked here (the C layer cannot see them).  Built once -- a blocking
+    host-to-device copy -- before any graph capture, then passed to
+    hq_group_contiguous_gemm_ptr_array on every call."""
     mode = _mode(mode)
-    rows, kc = a.shape
-    k = kc * (1 if mode == HQ_MXFP8 else 2)
     E = len(bs)
     if len(sfbs) != E:
         raise ValueError("bs and sfbs must have one tensor per group")
     for g in range(E):
         _need(bs[g], f"bs[{g}]", torch.uint8, n * code_cols(mode, k))
         _need(sfbs[g], f"sfbs[{g}]", torch.uint8, n * (k // group_size(mode)))
-        if not bs[g].is_contiguous() or not sfbs[g].is_contiguous():
-            raise ValueError(f"bs[{g}] and sfbs[{g}] must be contiguous")
         if bs[g].data_ptr() % 16 or sfbs[g].data_ptr() % 16:
             raise ValueError(f"bs[{g}] and sfbs[{g}] must be 16-byte aligned")
+    dev = bs[0].device if E else torch.device("cuda")
+    bp = torch.tensor([t.data_ptr() for t in bs], dtype=torch.int64).to(dev, non_blocking=False)
+    sp = torch.tensor([t.data_ptr() for t in sfbs], dtype=torch.int64).to(dev, non_blocking=False)
+    return bp, sp
+
+
+def hq_group_contiguous_gemm_ptr_array(mode, a, sfa, bs, sfbs, group_end, out, n, bias=None,
+                                       alpha=None, cu_limit=0):
+    """Grouped-contiguous GEMM whose group g uses its own weight tensors.
+    bs / sfbs are either lists of the per-expert tensors (the binding then
+    builds the address arrays with ptr_arrays: a host-to-device copy, so such
+    a call cannot be graph-captured) or the int64 device arrays that
+    ptr_arrays returned (no copy; capturable).  Returns the arrays used."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    if isinstance(bs, torch.Tensor):
+        bp, sp = bs, sfbs
+        E = bp.numel()
+        _need(bp, "b_ptrs", torch.int64, E)
+        _need(sp, "sfb_ptrs", torch.int64, E)
+    else:
+        bp, sp = ptr_arrays(mode, bs, sfbs, n, k)
+        E = len(bs)
     _need(a, "a", torch.uint8, rows * code_cols(mode, k))
     _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
     _need(group_end, "group_end", torch.int32, E)
     _need_out(out, rows * n)
     _need(bias, "bias", torch.bfloat16, E * n)
     _need(alpha, "alpha", torch.float32, E)
-    dev = a.device
-    bp = torch.tensor([t.data_ptr() for t in bs], dtype=torch.int64).to(dev, non_blocking=False)
-    sp = torch.tensor([t.data_ptr() for t in sfbs], dtype=torch.int64).to(dev, non_blocking=False)
     _check(load().hq_group_contiguous_gemm_ptr_array(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(bp), _p(sp),
                                                      _p(group_end), E, _p(bias), _p(alpha), _p(out),
                                                      rows, n, k, cu_limit))

@@ -138,12 +138,14 @@ __device__ __forceinline__ uint32_t mx_fp4x8(const float (&x)[8], uint32_t byte)
 // FP32 value to E2M1 exactly as e2m1_code (nearest even, saturating; checked
 // on the device over all 2^32 FP32 patterns).  For s in [2^-56, 2^56] the
 // quotients are formed with one shared reciprocal: r = 1/s from the hardware
-// reciprocal and one Newton step, then per value q = x r and two residual
-// corrections q += (x - s q) r, with FMAs.  These are the steps of the IEEE
-// FP32 division sequence (rcp, Newton, two corrections) when the divide-scale
-// steps leave both operands unscaled, which they do whenever the quotient
-// can round to anything but a zero or a saturated code (checked on the
-// device against x / s over every BF16 x and random FP32 x, for 2052 scales).
+// reciprocal and one Newton-Raphson step, then per value q = x r and two
+// FMA residual corrections q += (x - s q) r -- Markstein's correction scheme
+// for correctly rounded division (P. Markstein, "IA-64 and Elementary
+// Functions", 2000), which is also what AMD's open FP32 division expansion
+// does once its operand-scaling steps leave both operands unscaled.  That
+// holds whenever the quotient can round to anything but a zero or a
+// saturated code (checked on the device against x / s over every BF16 x and
+// random FP32 x, for 2052 scales).
 // The sign is copied from x, as the division gives it (x = -0 included).
 __device__ __forceinline__ uint32_t nv_fp4x8(const float (&x)[8], float s) {
   float q[8];

@@ -12,10 +12,22 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
 hipError_t launch_gemm_tiled(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev);
 bool tiled_supported(const GemmArgs& p);
 
-hipError_t launch_gemm(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+namespace {
+bool use_tiled(const GemmArgs& p) {
   const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
-  if (rows_hint > 16 && tiled_supported(p)) return launch_gemm_tiled(s, p, dev);
+  return rows_hint > 16 && tiled_supported(p);
+}
+}  // namespace
+
+hipError_t launch_gemm(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  if (use_tiled(p)) return launch_gemm_tiled(s, p, dev);
   return launch_gemm_direct(s, p, dev);
+}
+
+uint64_t gemm_workspace_bytes(const GemmArgs& p, const DeviceInfo& dev) {
+  if (!use_tiled(p)) return 0;
+  const SplitPlan sp = plan_split(p, dev);
+  return sp.kind == kSplitNone ? 0 : sp.bytes;
 }
 
 }  // namespace hq

@@ -36,7 +36,6 @@
 // K % 256 == 0 (FP4), at least two K steps; scale pointers 4-byte aligned; lda * 256 < 2^31;
 // n * 512 < 2^31.
 #include <atomic>
-#include <mutex>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -1029,32 +1028,70 @@ __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p) {
   }
 }
 
-// The library's stream-ordered pool for K-split workspaces, one per device:
-// freed blocks stay in the pool (no release threshold), so a repeated shape
-// reuses its memory without returning to the driver.
-hipMemPool_t workspace_pool(int device) {
-  static std::mutex mu;
-  static hipMemPool_t pools[64] = {};
-  static bool failed[64] = {};
-  if (device < 0 || device >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (pools[device] == nullptr && !failed[device]) {
-    hipMemPoolProps props = {};
-    props.allocType = hipMemAllocationTypePinned;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = device;
-    hipMemPool_t pool = nullptr;
-    if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
-      failed[device] = true;
-      (void)hipGetLastError();
-      return nullptr;
-    }
-    uint64_t keep = UINT64_MAX;
-    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-    pools[device] = pool;
-  }
-  return pools[device];
+// Compute units a launch may use (cu_limit caps them).
+int plan_cus(const GemmArgs& p, const DeviceInfo& dev) {
+  int cus = dev.num_cus;
+  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+  return cus;
 }
+
+}  // namespace
+
+// The split plan of a dense or batch call (uniform form) on the tiled kernel;
+// the launcher follows it when the caller's workspace holds sp.bytes.
+//  * Tail split (dense form): when the tiles fill some rounds of the grid and
+//    leave a last round at most half full, that round's tiles -- the last ones
+//    in the tile order, a rectangle of whole n-tile columns of the last block
+//    of 4 m-tiles -- run as a second, K-split launch on the rectangle, so they
+//    occupy the CUs with S times smaller units.  It pays only when a tile is
+//    long next to writing and summing its S partial planes: at least about
+//    110 us of matrix work per tail tile on a loaded chip, i.e. 40 FP4 steps,
+//    48 FP8 steps or 12 NVFP4 steps (whose FP16 products are slower).
+//  * K split (dense and batch forms) where the tiles cannot fill half of the
+//    CUs: S slices of at least 4 K steps each, S * tiles <= CUs, at most 8.
+SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
+  SplitPlan sp{};
+  sp.kind = kSplitNone;
+  if (p.form != kUniform || p.n * 1024 >= ((int64_t)1 << 31)) return sp;
+  const int64_t NT = (p.n + BN - 1) / BN;
+  const int64_t total_gm = (int64_t)p.num_groups * ((p.slot_rows + BM - 1) / BM);
+  const int64_t tiles = total_gm * NT;
+  const int cus = plan_cus(p, dev);
+  const int64_t grid_full = cus >= 8 ? cus - cus % 8 : cus;
+  const int64_t nk = p.lda / SROW;
+  const int64_t kTailMinSteps = p.mode == kNVFP4 ? 12 : (p.mode == kMXFP8 ? 48 : 40);
+  if (p.num_groups == 1 && tiles > grid_full && nk >= kTailMinSteps) {
+    const int64_t tail = tiles % grid_full;
+    const int64_t last_blk = (total_gm - 1) / 4;
+    const int64_t mb = total_gm - last_blk * 4;           // m-tiles of the last block
+    const int64_t cols = (tail + mb - 1) / mb;            // n-tile columns of the rectangle
+    int64_t S = cols * mb > 0 ? grid_full / (cols * mb) : 0;
+    if (S > nk / 4) S = nk / 4;
+    if (S > 8) S = 8;
+    if (tail > 0 && tail * 2 <= grid_full && cols < NT && S >= 2) {
+      sp.kind = kSplitTail;
+      sp.S = S;
+      sp.r0 = last_blk * 4 * BM;
+      sp.c0 = (NT - cols) * BN;
+      sp.rect_tiles = cols * mb;
+      sp.bytes = (uint64_t)(S * (p.m_rows - sp.r0) * (p.n - sp.c0) * 4);
+    }
+    return sp;
+  }
+  if (tiles * 2 <= cus && nk >= 8) {
+    int64_t S = cus / tiles;
+    if (S > nk / 4) S = nk / 4;
+    if (S > 8) S = 8;
+    if (S >= 2) {
+      sp.kind = kSplitAll;
+      sp.S = S;
+      sp.bytes = (uint64_t)(S * p.m_rows * p.n * 4);
+    }
+  }
+  return sp;
+}
+
+namespace {
 
 template <int FMT, bool GS>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
@@ -1080,100 +1117,66 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (p.form == kContiguous) gm_upper = (p.m_rows + BM - 1) / BM + p.num_groups;
   else gm_upper = (int64_t)p.num_groups * ((p.slot_rows + BM - 1) / BM);
   const int64_t tiles = gm_upper * NT;
-  int cus = dev.num_cus;
-  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
-
-  // Tail split (dense form): when the tiles fill some rounds of the grid and
-  // leave a last round at most half full, that round's tiles -- the last
-  // ones in the tile order, a rectangle of whole n-tile columns of the last
-  // block of 4 m-tiles -- run as a second, K-split launch on the rectangle,
-  // so they occupy the CUs with S times smaller units.  It pays only when a
-  // tile is long next to writing and summing its S partial planes: at least
-  // about 110 us of matrix work per tail tile on a loaded chip, i.e. 40 FP4
-  // steps, 48 FP8 steps or 12 NVFP4 steps (whose BF16 products are slower).
-  constexpr int64_t kTailMinSteps = FMT == kNV ? 12 : (FMT == 0 ? 48 : 40);
+  const int cus = plan_cus(p, dev);
   const int64_t grid_full = cus >= 8 ? cus - cus % 8 : cus;
-  const int64_t nk_all = p.lda / SROW;
-  if (p.form == kUniform && p.num_groups == 1 && tiles > grid_full && nk_all >= kTailMinSteps &&
-      p.n * 1024 < ((int64_t)1 << 31)) {
-    const int64_t tail = tiles % grid_full;
-    const int64_t total_gm = (p.m_rows + BM - 1) / BM;
-    const int64_t last_blk = (total_gm - 1) / 4;
-    const int64_t mb = total_gm - last_blk * 4;           // m-tiles of the last block
-    const int64_t cols = (tail + mb - 1) / mb;            // n-tile columns of the rectangle
-    int64_t S = cols * mb > 0 ? grid_full / (cols * mb) : 0;
-    if (S > nk_all / 4) S = nk_all / 4;
-    if (S > 8) S = 8;
-    if (tail > 0 && tail * 2 <= grid_full && cols < NT && S >= 2) {
-      const int64_t r0 = last_blk * 4 * BM, c0 = (NT - cols) * BN;
-      GemmArgs q2 = p;
-      q2.a = p.a + r0 * p.lda;
-      q2.sfa = p.sfa + r0 * p.ldsf;
-      q2.b = p.b + c0 * p.lda;
-      q2.sfb = p.sfb + c0 * p.ldsf;
-      q2.out = p.out + r0 * p.n + c0;
-      q2.bias = p.bias ? p.bias + c0 : nullptr;
-      q2.m_rows = p.m_rows - r0;
-      q2.slot_rows = q2.m_rows;
-      q2.n = p.n - c0;
-      q2.ldo = p.n;
-      q2.ksplit = (int32_t)S;
-      q2.tile_limit = 0;
-      hipMemPool_t pool = workspace_pool(dev.device);
-      void* ws = nullptr;
-      if (pool != nullptr &&
-          hipMallocFromPoolAsync(&ws, (size_t)(S * q2.m_rows * q2.n * 4), pool, s) == hipSuccess) {
-        q2.partial = static_cast<float*>(ws);
-        GemmArgs q1 = p;
-        q1.ksplit = 1;
-        q1.partial = nullptr;
-        q1.tile_limit = (int32_t)(tiles - cols * mb);
-        if (q1.out_f16)
-          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
-                             smem, s, q1);
-        else
-          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
-                             smem, s, q1);
-        hipError_t e = hipGetLastError();
-        if (e == hipSuccess) {
-          int64_t g2 = cols * mb * S;
-          if (g2 > grid_full) g2 = grid_full;
-          if (g2 >= 8) g2 -= g2 % 8;
-          hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
-          e = hipGetLastError();
-        }
-        if (e == hipSuccess) {
-          int64_t rgrid = (int64_t)cus * 4;
-          if (q2.m_rows < rgrid) rgrid = q2.m_rows;
-          hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q2);
-          e = hipGetLastError();
-        }
-        const hipError_t ef = hipFreeAsync(ws, s);
-        return e != hipSuccess ? e : ef;
-      }
-      (void)hipGetLastError();        // no workspace: run unsplit
+  // the split, if the plan has one and the caller's workspace holds it
+  const SplitPlan sp = plan_split(p, dev);
+  const bool split = sp.kind != kSplitNone && p.workspace != nullptr && p.workspace_bytes >= sp.bytes;
+
+  if (split && sp.kind == kSplitTail) {
+    // The last round's tiles -- a rectangle of whole n-tile columns of the
+    // last block of m-tiles -- run after the others as a K-split sub-problem
+    // (operand, scale, bias and output pointers offset to its corner; the
+    // split reduce writes with the full output's row stride).
+    const int64_t r0 = sp.r0, c0 = sp.c0;
+    GemmArgs q2 = p;
+    q2.a = p.a + r0 * p.lda;
+    q2.sfa = p.sfa + r0 * p.ldsf;
+    q2.b = p.b + c0 * p.lda;
+    q2.sfb = p.sfb + c0 * p.ldsf;
+    q2.out = p.out + r0 * p.n + c0;
+    q2.bias = p.bias ? p.bias + c0 : nullptr;
+    q2.m_rows = p.m_rows - r0;
+    q2.slot_rows = q2.m_rows;
+    q2.n = p.n - c0;
+    q2.ldo = p.n;
+    q2.ksplit = (int32_t)sp.S;
+    q2.tile_limit = 0;
+    q2.partial = static_cast<float*>(p.workspace);
+    GemmArgs q1 = p;
+    q1.ksplit = 1;
+    q1.partial = nullptr;
+    q1.tile_limit = (int32_t)(tiles - sp.rect_tiles);
+    if (q1.out_f16)
+      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
+                         smem, s, q1);
+    else
+      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
+                         smem, s, q1);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+      int64_t g2 = sp.rect_tiles * sp.S;
+      if (g2 > grid_full) g2 = grid_full;
+      if (g2 >= 8) g2 -= g2 % 8;
+      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
+      e = hipGetLastError();
     }
+    if (e == hipSuccess) {
+      int64_t rgrid = (int64_t)cus * 4;
+      if (q2.m_rows < rgrid) rgrid = q2.m_rows;
+      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q2);
+      e = hipGetLastError();
+    }
+    return e;
   }
 
-  // K split where the tiles cannot fill half of the CUs (dense and batch
-  // forms): S slices of at least 4 K steps each, S * tiles <= CUs, at most 8.
+  // K split of every tile (few tiles, long K)
   GemmArgs q = p;
   q.ksplit = 1;
   q.partial = nullptr;
-  const int64_t nk = p.lda / SROW;
-  if (p.form == kUniform && tiles * 2 <= cus && nk >= 8 && p.n * 1024 < ((int64_t)1 << 31)) {
-    int64_t S = cus / tiles;
-    if (S > nk / 4) S = nk / 4;
-    if (S > 8) S = 8;
-    hipMemPool_t pool = S >= 2 ? workspace_pool(dev.device) : nullptr;
-    void* ws = nullptr;
-    if (pool != nullptr &&
-        hipMallocFromPoolAsync(&ws, (size_t)(S * p.m_rows * p.n * 4), pool, s) == hipSuccess) {
-      q.ksplit = (int32_t)S;
-      q.partial = static_cast<float*>(ws);
-    } else {
-      (void)hipGetLastError();        // no workspace: run unsplit
-    }
+  if (split && sp.kind == kSplitAll) {
+    q.ksplit = (int32_t)sp.S;
+    q.partial = static_cast<float*>(p.workspace);
   }
   int64_t grid = cus;
   if (tiles * q.ksplit < grid) grid = tiles * q.ksplit;
@@ -1186,15 +1189,11 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   else
     hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
   hipError_t e = hipGetLastError();
-  if (q.ksplit > 1) {
-    if (e == hipSuccess) {
-      int64_t rgrid = (int64_t)cus * 4;
-      if (p.m_rows < rgrid) rgrid = p.m_rows;
-      hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q);
-      e = hipGetLastError();
-    }
-    const hipError_t ef = hipFreeAsync(q.partial, s);
-    if (e == hipSuccess) e = ef;
+  if (q.ksplit > 1 && e == hipSuccess) {
+    int64_t rgrid = (int64_t)cus * 4;
+    if (p.m_rows < rgrid) rgrid = p.m_rows;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)rgrid), dim3(256), 0, s, q);
+    e = hipGetLastError();
   }
   return e;
 }
@@ -1213,8 +1212,7 @@ hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo&
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
   }
   const int64_t tiles = ((p.m_rows + BM - 1) / BM + p.num_groups) * (p.h / 128);
-  int cus = dev.num_cus;
-  if (p.cu_limit > 0 && p.cu_limit < cus) cus = p.cu_limit;
+  const int cus = plan_cus(p, dev);
   int64_t grid = cus;
   if (tiles < grid) grid = tiles;
   if (grid >= 8) grid -= grid % 8;
@@ -1232,8 +1230,10 @@ hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo&
 bool tiled_supported(const GemmArgs& p);
 
 bool gemm_swiglu_supported(const GemmArgs& p) {
+  // the paired B loads reach h + 127 rows past a tile's first gate row with
+  // 32-bit byte offsets
   return p.mode == kMXFP8 && p.form == kContiguous && p.h > 0 && p.h % 128 == 0 && p.n == 2 * p.h &&
-         tiled_supported(p);
+         (p.h + 256) * p.lda < ((int64_t)1 << 31) && tiled_supported(p);
 }
 
 hipError_t launch_gemm_swiglu(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {

@@ -164,16 +164,24 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x, int
                   what);
 }
 
-hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
-                        const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
-                        const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
-                        int32_t cu_limit) {
+// A caller workspace: null with 0 bytes (unsplit), else 16-byte aligned.
+hq_status check_workspace(const void* ws, uint64_t bytes, const char* what) {
+  if (bytes > 0 && ws == nullptr) return fail(HQ_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", what);
+  if (ws != nullptr && !aligned16(ws)) return fail(HQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", what);
+  return HQ_OK;
+}
+
+hq_status hq_dense_gemm_ws(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                           const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                           const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
+                           int32_t cu_limit, void* workspace, uint64_t workspace_bytes) {
   const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
   mode &= ~(int32_t)HQ_OUT_FP16;
   GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, 1, "hq_dense_gemm"};
   bool noop;
   hq_status st = check_gemm(c, &noop);
   if (st != HQ_OK) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, c.what)) != HQ_OK) return st;
   if (noop) return ok();
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
@@ -183,13 +191,22 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
   p.num_groups = 1;
   p.m_rows = m;
   p.slot_rows = m;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
   return launched(hq::launch_gemm((hipStream_t)stream, p, dev), c.what);
 }
 
-hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
                         const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
-                        const float* alpha, uint16_t* out, int64_t batch, int64_t m, int64_t n,
-                        int64_t k, int32_t cu_limit) {
+                        const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
+                        int32_t cu_limit) {
+  return hq_dense_gemm_ws(stream, mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, cu_limit, nullptr, 0);
+}
+
+hq_status hq_batch_gemm_ws(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                           const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                           const float* alpha, uint16_t* out, int64_t batch, int64_t m, int64_t n,
+                           int64_t k, int32_t cu_limit, void* workspace, uint64_t workspace_bytes) {
   const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
   mode &= ~(int32_t)HQ_OUT_FP16;
   const char* what = "hq_batch_gemm";
@@ -200,6 +217,7 @@ hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
   bool noop;
   hq_status st = check_gemm(c, &noop);
   if (st != HQ_OK) return st;
+  if ((st = check_workspace(workspace, workspace_bytes, what)) != HQ_OK) return st;
   if (noop) return ok();
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
@@ -209,7 +227,44 @@ hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
   p.num_groups = (int32_t)batch;
   p.m_rows = batch * m;
   p.slot_rows = m;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
   return launched(hq::launch_gemm((hipStream_t)stream, p, dev), what);
+}
+
+hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                        const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                        const float* alpha, uint16_t* out, int64_t batch, int64_t m, int64_t n,
+                        int64_t k, int32_t cu_limit) {
+  return hq_batch_gemm_ws(stream, mode, a, sfa, b, sfb, bias, alpha, out, batch, m, n, k, cu_limit,
+                          nullptr, 0);
+}
+
+hq_status hq_gemm_workspace_size(int32_t mode, int64_t batch, int64_t m, int64_t n, int64_t k,
+                                 int32_t cu_limit, uint64_t* bytes) {
+  const char* what = "hq_gemm_workspace_size";
+  if (!bytes) return fail(HQ_ERR_NULL, "%s: bytes is required", what);
+  *bytes = 0;
+  mode &= ~(int32_t)HQ_OUT_FP16;
+  if (batch < 1 || batch > kI32) return fail(HQ_ERR_SHAPE, "%s: batch=%lld must be in [1, 2^31)", what, (long long)batch);
+  if (m < 0 || m > kI32 / batch) return fail(HQ_ERR_SHAPE, "%s: batch * m must be below 2^31", what);
+  // shape and mode checks of the GEMM calls (no pointers: bias / alpha as the mode wants)
+  static const uint8_t kAny[16] = {};
+  const float* alpha = mode == HQ_NVFP4 ? reinterpret_cast<const float*>(kAny) : nullptr;
+  GemmCheck c{mode, kAny, kAny, kAny, kAny, nullptr, alpha, kAny, batch * m, n, k, batch, what};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, n, k, cu_limit);
+  p.form = hq::kUniform;
+  p.num_groups = (int32_t)batch;
+  p.m_rows = batch * m;
+  p.slot_rows = m;
+  *bytes = hq::gemm_workspace_bytes(p, dev);
+  return ok();
 }
 
 hq_status hq_group_contiguous_gemm(void* stream, int32_t mode, const uint8_t* a,
@@ -289,6 +344,10 @@ hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode, cons
   bool noop;
   hq_status st = check_gemm(c, &noop);
   if (st != HQ_OK) return st;
+  // a tile's up rows lie h + 127 rows past its first gate row: their byte
+  // offsets from the tile's base must stay 32-bit
+  if ((h + 256) * k >= ((int64_t)1 << 31))
+    return fail(HQ_ERR_SHAPE, "%s: (h + 256) * k = %lld must be below 2^31", what, (long long)((h + 256) * k));
   if (noop) return ok();
   if (!group_end || !sf) return fail(HQ_ERR_NULL, "%s: group_end and sf are required", what);
   if (y_debug && !aligned16(y_debug)) return fail(HQ_ERR_ALIGN, "%s: y_debug must be 16-byte aligned", what);

@@ -64,6 +64,25 @@ struct GemmArgs {
   const uint64_t* b_ptrs;
   const uint64_t* sfb_ptrs;
   int32_t out_f16;      // out holds IEEE binary16 instead of BF16 (round to nearest even)
+  // Caller-owned FP32 workspace of a K-split dense / batch call (nullptr: the
+  // call runs unsplit).  The launcher splits only when workspace_bytes holds
+  // the plan's bytes (plan_split).
+  void* workspace;
+  uint64_t workspace_bytes;
+};
+
+// How a dense or batch call on the tiled kernel splits K (plan_split).
+enum SplitKind : int32_t {
+  kSplitNone = 0,
+  kSplitAll = 1,    // every tile's K steps in S slices
+  kSplitTail = 2,   // the last round's tiles (a rectangle at r0, c0) in S slices
+};
+struct SplitPlan {
+  int32_t kind;
+  int64_t S;
+  uint64_t bytes;        // FP32 workspace the split needs
+  int64_t r0, c0;        // kSplitTail: the rectangle's first row and column
+  int64_t rect_tiles;    // kSplitTail: its tiles
 };
 
 struct DeviceInfo {
@@ -81,6 +100,11 @@ hipError_t launch_swiglu_quant(hipStream_t s, int mode, const uint16_t* x, int64
                                int64_t slot_rows, const int32_t* valid, uint8_t* q,
                                uint8_t* sf, const float* gs, float* y_debug);
 hipError_t launch_gemm(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
+// The split plan of a tiled dense / batch launch, and the workspace bytes a
+// call of this shape uses (0 when it never splits: other forms, the direct
+// kernel).
+SplitPlan plan_split(const GemmArgs& args, const DeviceInfo& dev);
+uint64_t gemm_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
 // The gate|up GEMM with the SwiGLU + re-quant epilogue (args.h > 0); false
 // when the tiled kernel cannot take the shape (K, alignment).
 bool gemm_swiglu_supported(const GemmArgs& args);

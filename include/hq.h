@@ -12,14 +12,14 @@
  * Conventions shared by every call
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers (memory of the current HIP
- *    device).  The caller allocates and owns every buffer; the library keeps
- *    no pointer after a call returns and never synchronises the host.  The
- *    one allocation it makes is the FP32 workspace of a K-split dense or
- *    batch GEMM or of a dense GEMM's K-split last round (see hq_dense_gemm),
- *    taken from and returned to the
- *    library's own per-device stream-ordered pool inside the call's stream
- *    order.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
- *    stream) and is stream-ordered, so a call may be captured into a graph.
+ *    device).  The caller allocates and owns every buffer, the FP32
+ *    workspace of a K-split GEMM included (hq_dense_gemm_ws,
+ *    hq_batch_gemm_ws; the flashrt/fp4-gemm page's large-M tier, whose
+ *    workspace is caller-owned, allocated before graph capture and passed on
+ *    every replay).  The library allocates no memory, keeps no pointer after
+ *    a call returns and never synchronises the host.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and is stream-ordered
+ *    with no memset nodes, so a call may be captured into a graph.
  *  - BF16 values are passed as their uint16_t bit patterns.
  *  - Quantised operands are K-major and row-major:
  *        MXFP8: codes uint8 [rows, K]      (E4M3 "fn")
@@ -118,25 +118,56 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x,
  * alpha (device float[1]) is required in NVFP4 mode and rejected otherwise.
  * Accumulation is FP32 on the matrix cores; the output is rounded once to
  * BF16 (nearest even).  cu_limit > 0 caps the compute units used (<= 0: all).
- * When the output tiles cannot fill half of the compute units and K is long
- * (at least 8 K steps of 128 bytes per row), K is split into 2..8 contiguous
- * slices: each slice's FP32 partial products go to a workspace of
- * slices * m * n floats (batch: batch * m rows), a second kernel adds the
- * slices in order and applies bias / alpha, then rounds once to BF16.  The
- * workspace comes from the library's stream-ordered pool; if it cannot be
- * had, the call runs unsplit.  FP32 summation order (not the result's
- * contract) then differs from an unsplit call.
- * When the tiles fill whole rounds of the compute units and leave a last
- * round at most half full, and K is long (at least 48 MXFP8, 40 MXFP4 or 12
- * NVFP4 steps), the last round's tiles -- whole 256-column tiles of the last
- * 1024 rows or fewer -- are computed the same way, K-split into a workspace
- * of slices * rows * columns floats of that rectangle, after the other tiles.
+ * Every K step of a tile runs in one workgroup (no K split, no workspace);
+ * hq_dense_gemm_ws is the same call with a caller-owned workspace that lets
+ * K be split where the tiles cannot fill the chip.
  */
 hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
                         const uint8_t* sfa, const uint8_t* b,
                         const uint8_t* sfb, const uint16_t* bias,
                         const float* alpha, uint16_t* out, int64_t m,
                         int64_t n, int64_t k, int32_t cu_limit);
+
+/*
+ * hq_dense_gemm with a caller-owned FP32 workspace (the flashrt/fp4-gemm
+ * page's large-M tier: the workspace is allocated by the caller, before any
+ * graph capture, and passed on every call).  hq_gemm_workspace_size gives
+ * the bytes this shape uses; when workspace_bytes holds them the call may
+ * split K:
+ *  - when the output tiles cannot fill half of the compute units and K is
+ *    long (at least 8 K steps of 128 bytes per row), K is cut into 2..8
+ *    contiguous slices: each slice's FP32 partial products go to the
+ *    workspace (slices * m * n floats), a second kernel adds the slices in
+ *    order and applies bias / alpha, then rounds once to BF16;
+ *  - when the tiles fill whole rounds of the compute units and leave a last
+ *    round at most half full, and K is long (at least 48 MXFP8, 40 MXFP4 or
+ *    12 NVFP4 steps), the last round's tiles -- whole 256-column tiles of the
+ *    last 1024 rows or fewer -- are computed the same way, after the others,
+ *    with slices * rows * columns floats of that rectangle.
+ * With a NULL workspace, or fewer bytes than the shape uses, the call runs
+ * unsplit (as hq_dense_gemm).  A split changes the FP32 summation order, not
+ * the result's contract.  The workspace is scratch: its contents before and
+ * after the call mean nothing, and two calls in flight at once (on two
+ * streams) need two workspaces.  It must be 16-byte aligned
+ * (HQ_ERR_NULL for a NULL workspace with workspace_bytes > 0).
+ */
+hq_status hq_dense_gemm_ws(void* stream, int32_t mode, const uint8_t* a,
+                           const uint8_t* sfa, const uint8_t* b,
+                           const uint8_t* sfb, const uint16_t* bias,
+                           const float* alpha, uint16_t* out, int64_t m,
+                           int64_t n, int64_t k, int32_t cu_limit,
+                           void* workspace, uint64_t workspace_bytes);
+
+/*
+ * Workspace bytes that hq_dense_gemm_ws (batch == 1) or hq_batch_gemm_ws
+ * (batch items of m x n) uses for this shape, mode and cu_limit on the
+ * current device, written to *bytes; 0 when the shape never splits.  A host
+ * query (device properties only): nothing is launched.  Shape and mode
+ * errors as for the GEMM calls; HQ_ERR_DEVICE off gfx950.
+ */
+hq_status hq_gemm_workspace_size(int32_t mode, int64_t batch, int64_t m,
+                                 int64_t n, int64_t k, int32_t cu_limit,
+                                 uint64_t* bytes);
 
 /*
  * Batch GEMM (HALOps "GEMM" page, batch_gemm section): for every batch item
@@ -149,6 +180,16 @@ hq_status hq_batch_gemm(void* stream, int32_t mode, const uint8_t* a,
                         const uint8_t* sfb, const uint16_t* bias,
                         const float* alpha, uint16_t* out, int64_t batch,
                         int64_t m, int64_t n, int64_t k, int32_t cu_limit);
+
+/* hq_batch_gemm with a caller-owned workspace: the K split of
+ * hq_dense_gemm_ws (its first form: few tiles, long K) over all batch items,
+ * slices * batch * m * n floats; same workspace rules. */
+hq_status hq_batch_gemm_ws(void* stream, int32_t mode, const uint8_t* a,
+                           const uint8_t* sfa, const uint8_t* b,
+                           const uint8_t* sfb, const uint16_t* bias,
+                           const float* alpha, uint16_t* out, int64_t batch,
+                           int64_t m, int64_t n, int64_t k, int32_t cu_limit,
+                           void* workspace, uint64_t workspace_bytes);
 
 /*
  * Grouped-contiguous GEMM (HALOps "GEMM" page, group_contiguous_gemm section;
@@ -213,8 +254,8 @@ hq_status hq_group_contiguous_gemm_ptr_array(void* stream, int32_t mode,
  *   sf [m_total, h/32] UE8M0, y_debug (optional, device float [m_total, h]):
  *   the FP32 y of the written rows.
  *   h % 128 == 0 (h <= 2^20); k % 128 == 0 and k >= 256 (the tiled kernel's
- *   K step and two steps); sfa / sfb 4-byte aligned.
- * Rows not written keep their contents.  No workspace is allocated.
+ *   K step and two steps); (h + 256) * k < 2^31; sfa / sfb 4-byte aligned.
+ * Rows not written keep their contents.  No workspace is used.
  */
 hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode,
                                                 const uint8_t* a, const uint8_t* sfa,

@@ -165,3 +165,36 @@ def _permute(lib, x=A, T=8, row_bytes=4096, hidden=2048, scale=A, mode=0, ids=A,
 def test_permute_rejects_before_launch(lib, kw, code):
     assert _permute(lib, **kw) == code
     assert len(lib.hq_last_error()) > 0
+
+
+def test_workspace_calls_reject_before_launch(lib):
+    """The workspace forms validate their workspace before any device work:
+    a NULL workspace with a byte count, a misaligned one; the size query its
+    shape, mode and output pointer."""
+    d = lib.hq_dense_gemm_ws
+    assert d(None, 0, A, A, A, A, NUL, NUL, A, 64, 64, 64, 0, NUL, 1024) == -1
+    assert d(None, 0, A, A, A, A, NUL, NUL, A, 64, 64, 64, 0, MIS, 1024) == -3
+    assert d(None, 0, A, A, A, A, NUL, NUL, A, 64, 12, 64, 0, A, 1024) == -2
+    assert d(None, 0, A, A, A, A, NUL, NUL, A, 0, 64, 64, 0, NUL, 0) == 0
+    b = lib.hq_batch_gemm_ws
+    assert b(None, 0, A, A, A, A, NUL, NUL, A, 2, 64, 64, 64, 0, NUL, 16) == -1
+    assert b(None, 0, A, A, A, A, NUL, NUL, A, 2, 64, 64, 64, 0, MIS, 16) == -3
+    q = lib.hq_gemm_workspace_size
+    out = ctypes.c_uint64(99)
+    assert q(0, 1, 64, 64, 64, 0, NUL) == -1
+    assert q(0, 0, 64, 64, 64, 0, ctypes.byref(out)) == -2
+    assert q(0, 1, 64, 12, 64, 0, ctypes.byref(out)) == -2
+    assert q(0, 1, 64, 64, 48, 0, ctypes.byref(out)) == -2
+    assert q(7, 1, 64, 64, 64, 0, ctypes.byref(out)) == -4
+    assert q(0, 1, 0, 64, 64, 0, ctypes.byref(out)) == 0 and out.value == 0
+
+
+def test_gemm_swiglu_rejects_offsets_past_32_bits(lib):
+    """The gate|up GEMM with the SwiGLU epilogue reads a tile's up rows h + 127
+    rows past its first gate row with 32-bit offsets: shapes whose
+    (h + 256) * k reaches 2^31 are refused on the host (status -2, not a
+    device error), before any launch."""
+    f = lib.hq_group_contiguous_gemm_swiglu_quant
+    h, k = 32768, 65536
+    assert f(None, 0, A, A, A, A, A, 4, NUL, NUL, A, A, NUL, 1024, h, k, 0) == -2
+    assert "2^31" in hq.hq_last_error()

@@ -17,7 +17,9 @@ acceptance bound.
   largest, the first and the last expert, padding rows included.
 * Grouped-masked MXFP4, 64 experts x 256-row slots, K=7168, N=4096, with
   random bytes in the padded rows: sampled valid rows, and every padded
-  output row keeps its sentinel.
+  output row keeps its sentinel; and every valid row (all 9291) equals, bit
+  for bit, the grouped-contiguous GEMM on the gathered valid rows with
+  unpadded offsets (same kernel, same K order).
 """
 import numpy as np
 import pytest
@@ -113,7 +115,8 @@ def test_dense_qualification_grid_sampled(nk, m, mode):
     qb, sb, gb = hq.quantize(xb, mode)
     alpha = (ga * gb) if mode == "nvfp4" else None
     out = torch.full((m, n), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
-    hq.hq_dense_gemm(mode, qa, sa, qb, sb, out, alpha=alpha)
+    # with the workspace the shape asks for, as bench.py runs it (K split at M = 512, tail split at 4096)
+    hq.hq_dense_gemm(mode, qa, sa, qb, sb, out, alpha=alpha, workspace=hq.gemm_workspace(mode, m, n, k, device=dev))
     torch.cuda.synchronize()
     g_a = g_b = None
     if mode == "nvfp4":
@@ -200,5 +203,18 @@ def test_moe_masked_mxfp4_full_size_sampled():
         wrows = e * N + cols
         _check_block("mxfp4", out, rows, cols, d["a"][rows], d["b"].reshape(E * N, K)[wrows],
                      qa, qw, sa, sw, what=f"expert {e} (count {c})", b_rows=wrows)
-    del qa, qw, out
+    # the masked form equals the contiguous form on the gathered valid rows
+    valid_t = torch.from_numpy(np.flatnonzero(~pad)).to(dev)
+    T = int(counts.sum())
+    assert valid_t.numel() == T
+    ends = np.cumsum(counts).astype(np.int32)
+    qa_c, sa_c = qa[valid_t].contiguous(), sa[valid_t].contiguous()
+    out_c = torch.full((T, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_group_contiguous_gemm("mxfp4", qa_c, sa_c, qw.view(E, N, K // 2), sw.view(E, N, K // 32),
+                                U.dev_i32(ends, dev), out_c)
+    torch.cuda.synchronize()
+    same = torch.equal(out[valid_t].view(torch.int16), out_c.view(torch.int16))
+    ndiff = int((out[valid_t].view(torch.int16) != out_c.view(torch.int16)).sum())
+    assert same, f"masked != contiguous on the gathered valid rows: {ndiff} of {T * N} outputs differ"
+    del qa, qw, out, out_c, qa_c
     torch.cuda.empty_cache()

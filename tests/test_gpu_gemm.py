@@ -54,12 +54,18 @@ def _quant(bits, mode):
     return c, s, None
 
 
-def _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None, cu_limit=0):
+def _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None, cu_limit=0, ws=False):
+    """ws=True: with the workspace the shape asks for (which must be > 0: the
+    case is meant to split K)."""
     out = torch.full((m, n), 0, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    workspace = None
+    if ws:
+        workspace = hq.gemm_workspace(mode, m, n, k, cu_limit=cu_limit, device=dev)
+        assert workspace is not None, "the shape was expected to split K"
     hq.hq_dense_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
                      out, bias=None if bias is None else U.dev_bf16(bias, dev),
                      alpha=None if alpha is None else torch.tensor([alpha], dtype=torch.float32, device=dev),
-                     cu_limit=cu_limit)
+                     cu_limit=cu_limit, workspace=workspace)
     torch.cuda.synchronize()
     return U.host_bits(out)
 
@@ -152,7 +158,7 @@ def test_k_split_integer_exact(case):
     rng = np.random.default_rng(k + m)
     av, a, sfa = _int_operand(rng, m, k, mode, [-1, 0, 1])
     bv, b, sfb = _int_operand(rng, n, k, mode, [-1, 0, 1])
-    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None)
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None, ws=True)
     want = F.bf16_round((av @ bv.T).astype(np.float64))
     assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
 
@@ -167,9 +173,12 @@ def test_k_split_random(case):
     b, sfb, gb = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
     alpha = None if ga is None else np.float32(ga * gb)
     bias = synth.normal_bf16(rng, (n,), 0.1) if mode == "mxfp8" else None
-    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha)
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha, ws=True)
     want = G.dense_gemm(mode, a, sfa, b, sfb, bias, alpha)
     U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"k-split {mode}")
+    # without a workspace the same call runs unsplit, within the same bound
+    plain = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha)
+    U.assert_gemm_close(plain, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"unsplit {mode}")
 
 
 # A dense launch whose last round of tiles is at most half full: the leading
@@ -193,7 +202,8 @@ def test_tail_split_integer_exact(case):
     rng = np.random.default_rng(m + n + k)
     av, a, sfa = _int_operand(rng, m, k, mode, [-1, 0, 1])
     bv, b, sfb = _int_operand(rng, n, k, mode, [-1, 0, 1])
-    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None, cu_limit=cus)
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, alpha=1.0 if mode == "nvfp4" else None, cu_limit=cus,
+                     ws=True)
     want = F.bf16_round(av.astype(np.float64) @ bv.astype(np.float64).T)   # exact: |sums| <= k
     assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} differ"
 
@@ -209,9 +219,47 @@ def test_tail_split_random_with_bias_or_alpha(case):
     b, sfb, gb = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
     alpha = None if ga is None else np.float32(ga * gb)
     bias = synth.normal_bf16(rng, (n,), 0.1) if mode == "mxfp8" else None
-    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha, cu_limit=cus)
+    got = _dense_gpu(mode, a, sfa, b, sfb, m, n, k, dev, bias=bias, alpha=alpha, cu_limit=cus, ws=True)
     want = G.dense_gemm(mode, a, sfa, b, sfb, bias, alpha)
     U.assert_gemm_close(got, want, U.deq(mode, a, sfa), U.deq(mode, b, sfb), alpha, f"tail split {mode}")
+
+
+def test_workspace_size_query():
+    """The size query follows the split plan: S slices x rows x columns FP32
+    (K split: the whole output; tail split: the last round's rectangle), 0
+    where the call never splits (many tiles, short K, the direct kernel, the
+    grouped forms' shapes)."""
+    U.require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # (mxfp8, 300 x 520 x 8576): 2 x 3 = 6 tiles, 67 K steps -> S = min(cus / 6, 16, 8) = 8
+    assert hq.hq_gemm_workspace_size("mxfp8", 300, 520, 8576) == min(cus // 6, 8) * 300 * 520 * 4
+    # tail split of 520 x 1544 x 6144 on 16 CUs: a 2-column x 3-m-tile rectangle, S = 2
+    assert hq.hq_gemm_workspace_size("mxfp8", 520, 1544, 6144, cu_limit=16) == 2 * 520 * (1544 - 1280) * 4
+    assert hq.hq_gemm_workspace_size("mxfp8", 4096, 4096, 256) == 0         # short K
+    assert hq.hq_gemm_workspace_size("mxfp4", 16, 4096, 8192) == 0          # direct kernel
+    assert hq.hq_gemm_workspace_size("mxfp8", 100, 128, 4096, batch=3) == min(cus // 3, 8) * 300 * 128 * 4
+    assert hq.hq_gemm_workspace_size("mxfp8", 0, 128, 4096) == 0
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_workspace_size("mxfp8", 16, 12, 4096)                       # n % 8
+
+
+def test_too_small_workspace_runs_unsplit():
+    """A workspace smaller than the plan's is not used: the call runs unsplit
+    and gives the unsplit call's bits."""
+    dev = U.require_gpu()
+    mode, m, n, k = "mxfp8", 300, 520, 8576
+    rng = np.random.default_rng(77)
+    a, sfa, _ = _quant(synth.normal_bf16(rng, (m, k)), mode)
+    b, sfb, _ = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
+    need = hq.hq_gemm_workspace_size(mode, m, n, k)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=dev)
+    outs = []
+    for ws in (None, small):
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        hq.hq_dense_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
+                         out, workspace=ws)
+        outs.append(U.host_bits(out))
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_k_split_batch_with_bias():
@@ -225,9 +273,11 @@ def test_k_split_batch_with_bias():
     bias = synth.normal_bf16(rng, (Bn, n), 0.1)
     out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
     U.banner("k-split batch mxfp8")
+    ws = hq.gemm_workspace("mxfp8", m, n, k, batch=Bn, device=dev)
+    assert ws is not None
     hq.hq_batch_gemm("mxfp8", U.dev_u8(a, dev).view(Bn, m, k), U.dev_u8(sfa, dev).view(Bn, m, -1),
                      U.dev_u8(b, dev).view(Bn, n, k), U.dev_u8(sfb, dev).view(Bn, n, -1), out,
-                     bias=U.dev_bf16(bias, dev))
+                     bias=U.dev_bf16(bias, dev), workspace=ws)
     torch.cuda.synchronize()
     want = G.batch_gemm("mxfp8", a.reshape(Bn, m, k), sfa.reshape(Bn, m, -1), b.reshape(Bn, n, k),
                         sfb.reshape(Bn, n, -1), bias=bias)
@@ -248,9 +298,11 @@ def test_k_split_batch_nvfp4_alpha():
     alpha = np.array([ga * gb, np.float32(3.0) * ga * gb], np.float32)
     out = torch.empty(Bn, m, n, dtype=torch.bfloat16, device=dev)
     U.banner("k-split batch nvfp4")
+    ws = hq.gemm_workspace("nvfp4", m, n, k, batch=Bn, device=dev)
+    assert ws is not None
     hq.hq_batch_gemm("nvfp4", U.dev_u8(a, dev).view(Bn, m, -1), U.dev_u8(sfa, dev).view(Bn, m, -1),
                      U.dev_u8(b, dev).view(Bn, n, -1), U.dev_u8(sfb, dev).view(Bn, n, -1), out,
-                     alpha=torch.from_numpy(alpha).to(dev))
+                     alpha=torch.from_numpy(alpha).to(dev), workspace=ws)
     torch.cuda.synchronize()
     got = U.host_bits(out)
     for i in range(Bn):

@@ -41,11 +41,12 @@ def _assert_close16(got, want, a_deq, b_deq, alpha=None, what=""):
 
 
 def _dense16(mode, a, sfa, b, sfb, m, n, k, dev, bias=None, alpha=None, cu_limit=0):
+    """With the workspace the shape asks for, so K-split shapes split."""
     out = torch.full((m, n), SENTINEL, dtype=torch.int16, device=dev).view(torch.float16)
     hq.hq_dense_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev),
                      out, bias=None if bias is None else U.dev_bf16(bias, dev),
                      alpha=None if alpha is None else torch.tensor([alpha], dtype=torch.float32, device=dev),
-                     cu_limit=cu_limit)
+                     cu_limit=cu_limit, workspace=hq.gemm_workspace(mode, m, n, k, cu_limit=cu_limit, device=dev))
     torch.cuda.synchronize()
     return _host16(out)
 

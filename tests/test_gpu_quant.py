@@ -171,17 +171,43 @@ def test_quant_nvfp4_supplied_global_scale():
     _check("nvfp4", zeros, dev, what="all zero -> g = 1")
 
 
-def test_quant_large_activation_sample():
+def test_quant_large_activation_every_byte():
     """MoE activation quantisation at full size [65536, 4096] (MXFP8): every
-    scale byte and a sample of code rows against the oracle."""
+    code and every scale byte against the oracle (the oracle runs on chunks
+    of 4096 rows, several at a time)."""
+    from concurrent.futures import ThreadPoolExecutor
     dev = U.require_gpu()
-    rng = np.random.default_rng(31)
     m, k = 65536, 4096
-    U.banner("quant mxfp8 65536x4096 (sampled rows)")
+    U.banner("quant mxfp8 65536x4096 (every byte)")
     x = torch.randn(m, k, generator=torch.Generator(device=dev).manual_seed(31), device=dev).to(torch.bfloat16)
     q, sf, _ = hq.quantize(x, "mxfp8")
-    rows = np.sort(rng.choice(m, 512, replace=False))
-    xb = U.host_bits(x[torch.from_numpy(rows).to(dev)])
-    oc, os_ = Q.mx_quant_bf16(xb, "mxfp8")
-    assert np.array_equal(U.host_u8(sf[torch.from_numpy(rows).to(dev)]), os_)
-    assert np.array_equal(U.host_u8(q[torch.from_numpy(rows).to(dev)]), oc)
+    xb, qh, sh = U.host_bits(x), U.host_u8(q), U.host_u8(sf)
+    del x, q, sf
+    step = 4096
+
+    def chunk(r0):
+        oc, os_ = Q.mx_quant_bf16(xb[r0:r0 + step], "mxfp8")
+        return (np.array_equal(qh[r0:r0 + step], oc), np.array_equal(sh[r0:r0 + step], os_))
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(chunk, range(0, m, step)))
+    bad_codes = [i * step for i, (c, _) in enumerate(res) if not c]
+    bad_scales = [i * step for i, (_, s_) in enumerate(res) if not s_]
+    assert not bad_scales, f"scale bytes differ in the row chunks starting at {bad_scales}"
+    assert not bad_codes, f"codes differ in the row chunks starting at {bad_codes}"
+
+
+def test_quant_fp16_input_must_be_contiguous():
+    """A float16 x goes through the same contiguity and device checks as a
+    bfloat16 one: a transposed or broadcast view is refused before any call."""
+    dev = U.require_gpu()
+    x = torch.randn(64, 128, device=dev).to(torch.float16)
+    q = torch.empty(128, 64, dtype=torch.uint8, device=dev)
+    sf = torch.empty(128, 2, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        hq.hq_group_wise_quant("mxfp8", x.t(), q, sf)
+    row = torch.randn(1, 128, device=dev).to(torch.float16)
+    q2 = torch.empty(64, 128, dtype=torch.uint8, device=dev)
+    sf2 = torch.empty(64, 4, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        hq.hq_group_wise_quant("mxfp8", row.expand(64, 128), q2, sf2)
