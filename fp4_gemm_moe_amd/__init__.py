@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "HQ_MXFP8", "HQ_MXFP4", "HQ_NVFP4", "HQ_GS_INPUT", "HQ_IN_FP16", "HQ_OUT_FP16", "HQError",
     "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm", "hq_gemm_workspace_size",
-    "gemm_workspace", "ptr_arrays",
+    "gemm_workspace", "ptr_arrays", "hq_dense_gemm_scratch", "HQ_SCRATCH_BYTES",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
@@ -41,7 +41,7 @@ MODES = {"mxfp8": HQ_MXFP8, "mxfp4": HQ_MXFP4, "nvfp4": HQ_NVFP4,
 
 EXPORTED_SYMBOLS = (
     "hq_last_error", "hq_group_wise_quant", "hq_dense_gemm", "hq_batch_gemm",
-    "hq_dense_gemm_ws", "hq_batch_gemm_ws", "hq_gemm_workspace_size",
+    "hq_dense_gemm_ws", "hq_batch_gemm_ws", "hq_gemm_workspace_size", "hq_dense_gemm_scratch",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm",
@@ -77,6 +77,7 @@ _SIGS = {
     "hq_batch_gemm_ws": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I32, _VP,
                           _U64], _I32),
     "hq_gemm_workspace_size": ([_I32, _I64, _I64, _I64, _I64, _I32, ctypes.POINTER(ctypes.c_uint64)], _I32),
+    "hq_dense_gemm_scratch": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                   _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm_ptr_array": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
@@ -236,6 +237,21 @@ def hq_dense_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, m=None, n=No
     wp, wb = _workspace(workspace)
     _check(load().hq_dense_gemm_ws(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
                                    _p(bias), _p(alpha), _p(out), m, n, k, cu_limit, wp, wb))
+
+
+HQ_SCRATCH_BYTES = 32 << 20
+
+
+def hq_dense_gemm_scratch(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0):
+    """hq_dense_gemm_ws whose K-split workspace is the library's static
+    scratch (HQ_SCRATCH_BYTES per GPU): allocates nothing; shapes whose split
+    needs more are refused; calls overlapping on one GPU race."""
+    mode = _mode(mode)
+    m, n = out.shape[0], out.shape[-1]
+    k = a.shape[-1] * (1 if mode == HQ_MXFP8 else 2)
+    _gemm_common(mode, a, sfa, b, sfb, out, bias, alpha, m, n, k, 1, 1)
+    _check(load().hq_dense_gemm_scratch(_stream(a), _out_mode(mode, out), _p(a), _p(sfa), _p(b), _p(sfb),
+                                        _p(bias), _p(alpha), _p(out), m, n, k, cu_limit))
 
 
 def hq_batch_gemm(mode, a, sfa, b, sfb, out, bias=None, alpha=None, cu_limit=0, workspace=None):

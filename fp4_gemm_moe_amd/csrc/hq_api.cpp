@@ -81,6 +81,36 @@ hq_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// ---------------------------------------------------------------- scratch
+// The K-split workspace of hq_dense_gemm_scratch: a fixed device array of
+// HQ_SCRATCH_BYTES, one copy per GPU, held until the process ends.  In host
+// code `scratch` only names the symbol: its device address on the current
+// GPU comes from hipGetSymbolAddress, once per device, and only that address
+// is handed to kernels.  Every call on a GPU shares its copy (calls that
+// overlap on one GPU race); nothing in it has to start at zero, since a
+// K-split launch writes every partial value before its reduce reads it.
+static __device__ __align__(256) uint8_t scratch[HQ_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// The current device's scratch address (dev.device current); nullptr and a
+// message when the symbol cannot be resolved.
+void* scratch_address(const hq::DeviceInfo& dev) {
+  if (dev.device < 0 || dev.device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev.device] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(HQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev.device, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev.device] = ptr;
+  }
+  return g_scratch_ptr[dev.device];
+}
+
 // ---------------------------------------------------------------- GEMM checks
 struct GemmCheck {
   int32_t mode;
@@ -201,6 +231,39 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a, const uint
                         const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
                         int32_t cu_limit) {
   return hq_dense_gemm_ws(stream, mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, cu_limit, nullptr, 0);
+}
+
+hq_status hq_dense_gemm_scratch(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                                const uint8_t* b, const uint8_t* sfb, const uint16_t* bias,
+                                const float* alpha, uint16_t* out, int64_t m, int64_t n, int64_t k,
+                                int32_t cu_limit) {
+  const bool out_f16 = (mode & HQ_OUT_FP16) != 0;   // binary16 output
+  mode &= ~(int32_t)HQ_OUT_FP16;
+  GemmCheck c{mode, a, sfa, b, sfb, bias, alpha, out, m, n, k, 1, "hq_dense_gemm_scratch"};
+  bool noop;
+  hq_status st = check_gemm(c, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, bias, alpha, out, n, k, cu_limit);
+  p.out_f16 = out_f16 ? 1 : 0;
+  p.form = hq::kUniform;
+  p.num_groups = 1;
+  p.m_rows = m;
+  p.slot_rows = m;
+  const uint64_t need = hq::gemm_workspace_bytes(p, dev);
+  if (need > (uint64_t)HQ_SCRATCH_BYTES)
+    return fail(HQ_ERR_SHAPE, "%s: this shape's K split needs %llu bytes of workspace, more than the %llu "
+                "of the library's scratch (use hq_dense_gemm_ws with a workspace of that size, or hq_dense_gemm)",
+                c.what, (unsigned long long)need, (unsigned long long)HQ_SCRATCH_BYTES);
+  if (need > 0) {
+    void* ptr = scratch_address(dev);
+    if (ptr == nullptr) return HQ_ERR_DEVICE;
+    p.workspace = ptr;
+    p.workspace_bytes = (uint64_t)HQ_SCRATCH_BYTES;
+  }
+  return launched(hq::launch_gemm((hipStream_t)stream, p, dev), c.what);
 }
 
 hq_status hq_batch_gemm_ws(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,

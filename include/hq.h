@@ -159,6 +159,26 @@ hq_status hq_dense_gemm_ws(void* stream, int32_t mode, const uint8_t* a,
                            void* workspace, uint64_t workspace_bytes);
 
 /*
+ * hq_dense_gemm_ws for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * K-split workspace is the library's own scratch array of HQ_SCRATCH_BYTES
+ * per GPU (a static device array, resolved once per device on first use and
+ * held until the process ends); the call allocates nothing.  Same arguments,
+ * result and split plan as hq_dense_gemm_ws given a workspace of
+ * HQ_SCRATCH_BYTES.  A shape whose plan needs more than HQ_SCRATCH_BYTES
+ * (hq_gemm_workspace_size) is refused with HQ_ERR_SHAPE before any launch.
+ * Every call on one GPU uses the same scratch: calls that may overlap on a
+ * GPU (several streams, several host threads) race and must be serialised
+ * by the caller; a call's scratch contents are meaningless afterwards.
+ */
+#define HQ_SCRATCH_BYTES (32u << 20)
+hq_status hq_dense_gemm_scratch(void* stream, int32_t mode, const uint8_t* a,
+                                const uint8_t* sfa, const uint8_t* b,
+                                const uint8_t* sfb, const uint16_t* bias,
+                                const float* alpha, uint16_t* out, int64_t m,
+                                int64_t n, int64_t k, int32_t cu_limit);
+
+/*
  * Workspace bytes that hq_dense_gemm_ws (batch == 1) or hq_batch_gemm_ws
  * (batch items of m x n) uses for this shape, mode and cu_limit on the
  * current device, written to *bytes; 0 when the shape never splits.  A host
