@@ -26,13 +26,18 @@ from . import formats as F
 from . import quant as Q
 
 
+def swiglu_values_f64(gate, up):
+    """y = up * gate / (1 + exp(-gate)) of real gate / up values, float64."""
+    gate = np.asarray(gate, np.float64)
+    up = np.asarray(up, np.float64)
+    with np.errstate(over="ignore"):
+        return up * gate / (1.0 + np.exp(-gate))
+
+
 def swiglu_f64(x_bits, h):
     """y[r, j] = up[r, j] * gate[r, j] / (1 + exp(-gate[r, j])) in float64."""
     x = F.bf16_decode(x_bits)
-    gate = x[:, :h]
-    up = x[:, h:2 * h]
-    with np.errstate(over="ignore"):
-        return up * gate / (1.0 + np.exp(-gate))
+    return swiglu_values_f64(x[:, :h], x[:, h:2 * h])
 
 
 def processed_rows(rows, group_end=None, slot_rows=0, valid=None, num_groups=0):
