@@ -23,6 +23,8 @@ ID runs one of them alone, e.g. under a profiler):
   d2  dense MXFP4 / NVFP4, N = 17408, K = 5120, M in {1, 512, 4096} (caller
       workspace: K split at M = 512, tail split at 4096)
   d4  grouped-masked MXFP4, 64 experts x 256-row slots, K = 7168, N = 4096
+  n3  the backward grouped GEMM with the dSwiGLU epilogue, MXFP8, the MoE shape
+      (32 experts, 65536 routed rows, K = 4096, N = 1536, C / D [rows, 3072])
   d5  quantisation bandwidth: MXFP4 [16384, 7168], NVFP4 [4096, 17408] (global
       scale supplied, and with the amax pass)
 each with its time, achieved rate, roofline fraction and, where affordable,
@@ -550,7 +552,7 @@ def _rec(cid, workload, us, flops=None, bytes_=None, bound="mfma", peak_key="mxf
 CONFIG_IDS = ["d0", "d1_batch", "d1_batch_bias", "d1_mxfp4",
               "d2_mxfp4_M1", "d2_mxfp4_M512", "d2_mxfp4_M4096",
               "d2_nvfp4_M1", "d2_nvfp4_M512", "d2_nvfp4_M4096",
-              "d4", "d5_mxfp4", "d5_nvfp4", "d5_nvfp4_amax"]
+              "d4", "n3", "d5_mxfp4", "d5_nvfp4", "d5_nvfp4_amax"]
 
 
 def run_configs(torch, hq, synth, only=None, oracle=True):
@@ -694,6 +696,36 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
                   bytes_=bytes_, bound="hbm", mean_us=round(mean, 2), routed_rows=T,
                   mfma_frac=round(2.0 * T * N * K / (med * 1e-6) / 1e12 / PEAK_TFLOPS["mxfp4"], 4)))
         del aq, asf, wq, wsf, out, d
+        torch.cuda.empty_cache()
+
+    # n3: the backward grouped GEMM with the dSwiGLU epilogue at the MoE shape
+    if want("n3"):
+        d = synth.moe_dglu_backward(threads=16)
+        counts, ends = d["counts"], d["group_end"]
+        R, K, N, E = int(ends[-1]), d["K"], d["N"], len(counts)
+        T = int(counts.sum())
+        qa, sa, _ = hq.quantize(_dev_bf16(torch, d["a"], dev), "mxfp8")
+        w = _dev_bf16(torch, d["b"].reshape(E * N, K), dev)
+        qw, sw, _ = hq.quantize(w, "mxfp8")
+        del w
+        qw, sw = qw.view(E, N, K), sw.view(E, N, K // 32)
+        c = _dev_bf16(torch, d["c"], dev)
+        ge = torch.from_numpy(ends.astype(np.int32)).to(dev)
+        prob = torch.from_numpy(d["prob"]).to(dev)
+        al, be = torch.from_numpy(d["alpha"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+        dprob = torch.zeros(R, dtype=torch.float32, device=dev)
+        dout = torch.empty(R, 2 * N, dtype=torch.bfloat16, device=dev)
+        med, mean = _launch_us(torch, [lambda: hq.hq_group_contiguous_gemm_dswiglu(
+            "mxfp8", qa, sa, qw, sw, ge, c, prob, dprob, dout, alpha=al, beta=be)], reps=20)
+        flops = 2.0 * T * N * K
+        # A codes + scales and C, D of the valid rows, the experts' weights, prob and dprob
+        bytes_ = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * T * 2 * N * 2 + 12 * T
+        t_ideal = max(flops / (PEAK_TFLOPS["mxfp8"] * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9))
+        emit(_rec("n3", "moe_bwd_dswiglu_mxfp8_E32_T65536_K4096_N1536", med, flops=flops, bytes_=bytes_,
+                  bound="mfma", mean_us=round(mean, 2), routed_rows=T,
+                  hbm_frac=round(bytes_ / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
+                  roofline_frac=round(t_ideal / (med * 1e-6), 3)))
+        del qa, qw, c, dout, dprob, d
         torch.cuda.empty_cache()
 
     # d5: quantisation bandwidth (input ring of >= 1 GB: past the MALL)

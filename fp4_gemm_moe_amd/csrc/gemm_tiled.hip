@@ -456,8 +456,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // p.out_f16); kEpiSplit (the launch has a
 // K split, p.ksplit > 1) writes FP32 partial tiles; kEpiSwiglu (MXFP8, p.h > 0,
 // PAIRED B rows) applies SwiGLU and the MXFP8 re-quant and writes codes and
-// scales of y instead of the gate|up output.
-constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3;
+// scales of y instead of the gate|up output; kEpiDswiglu (the backward
+// GEMM, grouped-contiguous) applies the dSwiGLU derivative to R with the
+// forward activations C and writes D and the dprob row sums.
+constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4;
 
 template <int FMT, int EPI, bool GS>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
@@ -466,7 +468,10 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   constexpr int FI = C::FI, FJ = C::FJ, WTM = C::WTM, WTN = C::WTN, WGN = C::WGN;
   // vector-memory operations of the epilogue (at least; the waits below rely
   // on no fewer being issued after the next tile's loads)
-  constexpr int kStores = EPI == kEpiSwiglu ? FI * 2 * 3 : C::kStores;
+  // (kEpiDswiglu issues FI * FJ * 4 stores after its loads of C; a smaller
+  // count only makes the waits stricter, and vmcnt holds at most 63)
+  constexpr int kStores = EPI == kEpiSwiglu ? FI * 2 * 3 : (EPI == kEpiDswiglu ? 32 : C::kStores);
+  static_assert(EPI != kEpiDswiglu || FI * FJ * 4 >= 32, "the dSwiGLU epilogue issues at least 32 stores");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TiledTable tt;
 
@@ -805,6 +810,104 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
             __builtin_amdgcn_raw_buffer_store_b128(o, prsrc, (int)off, 0, 0);
           }
         }
+    } else if constexpr (EPI == kEpiDswiglu) {
+      // ---- dSwiGLU epilogue (cuDNN FE "Grouped GEMM + dGLU (SM100)", Step 2,
+      // dSwiGLU).  Fragment (i, j) of this wave holds R columns
+      // nb = n0 + wn WTN + 32 j + [0, 32) -- one 32-column block pair of C and D,
+      // columns 2 nb (input) and 2 nb + 32 (gate) -- for rows 32 i + [0, 32):
+      // lane l, register 4b + r is row l % 32, column 8b + 4(l/32) + r; lanes
+      // l and l ^ 32 swap quads so that each lane owns two runs of 8
+      // consecutive columns, 16e + 8(l/32) .. + 7.  With X = beta C (the
+      // group's beta) and R times the group's alpha^2:
+      //   s = sigmoid(gate), swish = gate s,
+      //   D[input] = R prob swish,  D[gate] = R prob input s (1 + gate (1 - s)),
+      //   dprob[row] += sum of swish input R over the row's columns
+      // in FP32, D rounded once to BF16.  The row sums of a wave's columns are
+      // added to dprob with one atomic per row and wave.  Rows past the tile's
+      // rows and columns past n fall outside the buffer bounds (loads read 0,
+      // stores are dropped) and add nothing to dprob.
+      const int64_t C2 = 2 * p.n;
+      const int64_t trows = tl.row_end - tl.row0;
+      const uint32_t cbytes = ufirst((uint32_t)(trows * C2 * 2));
+      const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(uniform_ptr(reinterpret_cast<const uint8_t*>(p.c_in + tl.row0 * C2))), (short)0,
+          (int)cbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(uniform_ptr(reinterpret_cast<const uint8_t*>(p.d_out + tl.row0 * C2))), (short)0,
+          (int)cbytes, 0x00020000);
+      const float al = p.alpha != nullptr ? p.alpha[tl.g] : 1.0f;
+      const float a2 = al * al;
+      const float be = p.beta != nullptr ? p.beta[tl.g] : 1.0f;
+      // lane-derived offsets from an opaque copy of the lane id (computed
+      // here, not kept live through the K loop)
+      int le;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(le) : "v"(lane));
+      const int he = le >> 5, re = le & 31;
+      typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int64_t mr = wm * WTM + i * 32 + re;             // row within the tile
+        const bool row_ok = mr < trows;
+        const float pr = row_ok ? p.prob[tl.row0 + mr] : 0.0f;
+        // the C runs of every fragment of the row: input and gate, 16 bytes each
+        v4u cin[FJ][2], cgt[FJ][2];
+        uint32_t coff[FJ][2];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          const int64_t nb = tl.n0 + wn * WTN + j * 32;        // first R column of the pair
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int64_t col = 2 * nb + 16 * e + 8 * he;       // C / D column of the input run
+            coff[j][e] = nb < p.n ? (uint32_t)((mr * C2 + col) * 2) : 0x80000000u;
+            cin[j][e] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)coff[j][e], 0, 0);
+            cgt[j][e] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(coff[j][e] + 64u), 0, 0);
+          }
+        }
+        float dsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float run[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * e + r]),
+                                                               __float_as_uint(acc[i][j][8 * e + 4 + r]), false, false);
+              run[r] = __uint_as_float(sw[0]);
+              run[4 + r] = __uint_as_float(sw[1]);
+            }
+            uint32_t din[4], dgt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float dv[2], gv[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int t = 2 * q + u;
+                const uint32_t wi = cin[j][e][q], wg = cgt[j][e][q];
+                const float xi = be * (u == 0 ? bf16_lo(wi) : bf16_hi(wi));
+                const float xg = be * (u == 0 ? bf16_lo(wg) : bf16_hi(wg));
+                const float r = run[t] * a2;
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-xg * 1.4426950408889634f));
+                const float swish = xg * sg;
+                const float rp = r * pr;
+                dv[u] = rp * swish;
+                gv[u] = rp * xi * sg * (1.0f + xg * (1.0f - sg));
+                dsum += coff[j][e] != 0x80000000u ? swish * xi * r : 0.0f;
+              }
+              din[q] = pack_bf16x2(dv[0], dv[1]);
+              dgt[q] = pack_bf16x2(gv[0], gv[1]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v4u{din[0], din[1], din[2], din[3]}, drs, (int)coff[j][e], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v4u{dgt[0], dgt[1], dgt[2], dgt[3]}, drs,
+                                                   (int)(coff[j][e] + 64u), 0, 0);
+          }
+        }
+        // the row's other 16 columns of every fragment are in lane l ^ 32
+        dsum += __shfl_xor(dsum, 32, 64);
+        if (row_ok && he == 0) unsafeAtomicAdd(p.dprob + tl.row0 + mr, dsum);
+        // one fragment row at a time (all rows' loads at once run out of registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else if constexpr (EPI == kEpiSwiglu) {
       // ---- SwiGLU + MXFP8 re-quant epilogue.  Fragment j < 2 of this wave
       // holds gate and fragment j + 2 up of the same 32 y columns
@@ -1225,9 +1328,48 @@ hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo&
   return hipGetLastError();
 }
 
+// The backward grouped GEMM with the dSwiGLU epilogue: grouped-contiguous,
+// MXFP8 or MXFP4, 256-column n-tiles of R.
+template <int FMT, bool GS>
+hipError_t launch_dswiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  const int smem = Lay<FMT, GS>::SMEM;
+  static std::atomic<bool> attr_set[64];
+  const bool cached = dev.device >= 0 && dev.device < 64;
+  if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiDswiglu, GS>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    if (cached) attr_set[dev.device].store(true, std::memory_order_release);
+  }
+  const int64_t tiles = ((p.m_rows + BM - 1) / BM + p.num_groups) * ((p.n + BN - 1) / BN);
+  const int cus = plan_cus(p, dev);
+  int64_t grid = cus;
+  if (tiles < grid) grid = tiles;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid < 1) grid = 1;
+  GemmArgs q = p;
+  q.ksplit = 1;
+  q.partial = nullptr;
+  q.tile_limit = 0;
+  hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiDswiglu, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s,
+                     q);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool tiled_supported(const GemmArgs& p);
+
+bool gemm_dswiglu_supported(const GemmArgs& p) {
+  return (p.mode == kMXFP8 || p.mode == kMXFP4) && p.form == kContiguous && p.n % 32 == 0 &&
+         p.n * 1024 < ((int64_t)1 << 31) && tiled_supported(p);
+}
+
+hipError_t launch_gemm_dswiglu(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  const bool gs = p.ldsf % 16 == 0;
+  if (p.mode == kMXFP8) return gs ? launch_dswiglu_cfg<0, true>(s, p, dev) : launch_dswiglu_cfg<0, false>(s, p, dev);
+  return gs ? launch_dswiglu_cfg<4, true>(s, p, dev) : launch_dswiglu_cfg<4, false>(s, p, dev);
+}
 
 bool gemm_swiglu_supported(const GemmArgs& p) {
   // the paired B loads reach h + 127 rows past a tile's first gate row with

@@ -435,6 +435,52 @@ hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode, cons
   return launched(hq::launch_gemm_swiglu((hipStream_t)stream, p, dev), what);
 }
 
+hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uint8_t* a,
+                                           const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                           const int32_t* group_end, int32_t num_groups,
+                                           const uint16_t* c, const float* alpha, const float* beta,
+                                           const float* prob, float* dprob, uint16_t* d,
+                                           int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
+  const char* what = "hq_group_contiguous_gemm_dswiglu";
+  if (mode != HQ_MXFP8 && mode != HQ_MXFP4)
+    return fail(HQ_ERR_MODE, "%s: MXFP8 or MXFP4 codes only (got %d)", what, mode);
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(HQ_ERR_SHAPE, "%s: num_groups=%d must be in [1, 1024]", what, num_groups);
+  if (n % 32 != 0) return fail(HQ_ERR_SHAPE, "%s: n=%lld must be a multiple of 32", what, (long long)n);
+  if (n > 0 && n * 1024 >= ((int64_t)1 << 31))
+    return fail(HQ_ERR_SHAPE, "%s: n=%lld too large (n * 1024 must be below 2^31)", what, (long long)n);
+  // alpha here is the per-group GEMM scale (entering squared), not the NVFP4 alpha
+  GemmCheck cc{mode, a, sfa, b, sfb, nullptr, nullptr, d, m_total, n, k, num_groups, what};
+  bool noop;
+  hq_status st = check_gemm(cc, &noop);
+  if (st != HQ_OK) return st;
+  if (noop) return ok();
+  if (!group_end || !c || !prob || !dprob) return fail(HQ_ERR_NULL, "%s: group_end, c, prob and dprob are required", what);
+  if (!aligned16(c)) return fail(HQ_ERR_ALIGN, "%s: c must be 16-byte aligned", what);
+  if ((reinterpret_cast<uintptr_t>(prob) | reinterpret_cast<uintptr_t>(dprob)) & 3u)
+    return fail(HQ_ERR_ALIGN, "%s: prob and dprob must be 4-byte aligned", what);
+  hq::GemmArgs p = make_args(mode, a, sfa, b, sfb, nullptr, alpha, nullptr, n, k, cu_limit);
+  p.form = hq::kContiguous;
+  p.group_end = group_end;
+  p.num_groups = num_groups;
+  p.m_rows = m_total;
+  p.slot_rows = 0;
+  p.c_in = c;
+  p.beta = beta;
+  p.prob = prob;
+  p.dprob = dprob;
+  p.d_out = d;
+  if (!hq::gemm_dswiglu_supported(p)) {
+    if ((reinterpret_cast<uintptr_t>(sfa) | reinterpret_cast<uintptr_t>(sfb)) & 3)
+      return fail(HQ_ERR_ALIGN, "%s: sfa and sfb must be 4-byte aligned", what);
+    return fail(HQ_ERR_SHAPE, "%s: k=%lld must be a multiple of the K step (128 MXFP8, 256 MXFP4) of at least "
+                "two steps", what, (long long)k);
+  }
+  hq::DeviceInfo dev;
+  if ((st = current_device(&dev)) != HQ_OK) return st;
+  return launched(hq::launch_gemm_dswiglu((hipStream_t)stream, p, dev), what);
+}
+
 hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
                                const uint8_t* b, const uint8_t* sfb, const int32_t* masked_m,
                                int32_t num_groups, int64_t max_m_per_group, const uint16_t* bias,

@@ -69,6 +69,15 @@ struct GemmArgs {
   // the plan's bytes (plan_split).
   void* workspace;
   uint64_t workspace_bytes;
+  // Backward GEMM with the dSwiGLU epilogue (kContiguous, tiled kernel): R =
+  // alpha[g]^2 A B^T combined with the forward activations c_in [m_rows, 2n]
+  // BF16 (32-column input / gate blocks), scaled by beta[g], and prob
+  // [m_rows]; writes d_out [m_rows, 2n] BF16 and adds row sums to dprob.
+  const uint16_t* c_in;
+  const float* beta;
+  const float* prob;
+  float* dprob;
+  uint16_t* d_out;
 };
 
 // How a dense or batch call on the tiled kernel splits K (plan_split).
@@ -108,6 +117,10 @@ uint64_t gemm_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
 // The gate|up GEMM with the SwiGLU + re-quant epilogue (args.h > 0); false
 // when the tiled kernel cannot take the shape (K, alignment).
 bool gemm_swiglu_supported(const GemmArgs& args);
+// The backward grouped GEMM with the dSwiGLU epilogue (args.c_in / d_out);
+// false when the tiled kernel cannot take the shape.
+bool gemm_dswiglu_supported(const GemmArgs& args);
+hipError_t launch_gemm_dswiglu(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
 hipError_t launch_gemm_swiglu(hipStream_t s, const GemmArgs& args, const DeviceInfo& dev);
 hipError_t launch_permute(hipStream_t s, const uint8_t* x, int64_t tokens, int64_t row_bytes,
                           int64_t hidden, const void* scale, int32_t scale_mode, const int64_t* ids,

@@ -288,6 +288,44 @@ hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode,
                                                 int32_t cu_limit);
 
 /*
+ * Backward block-scaled grouped GEMM with the dSwiGLU epilogue (cuDNN FE
+ * "Grouped GEMM + dGLU (SM100)": the compact-gradient equation
+ * R_g = alpha_g^2 A_g B_g^T, X_g = beta_g C_g; Step 1, the block-scaled
+ * grouped GEMM; Step 2, the dGLU epilogue for dSwiGLU).  For every row m of
+ * group g (rows [group_end[g-1], group_end[g]), as hq_group_contiguous_gemm)
+ * and R column n = 32 j + t, with input = X[m, 64 j + t],
+ * gate = X[m, 64 j + 32 + t], s = sigmoid(gate), swish = gate s:
+ *   d[m, 64 j + t]      = R[m, n] prob[m] swish
+ *   d[m, 64 j + 32 + t] = R[m, n] prob[m] input s (1 + gate (1 - s))
+ *   dprob[m]           += sum over n of swish input R[m, n]
+ * in FP32, d rounded once to BF16.
+ *   mode HQ_MXFP8 or HQ_MXFP4; a [m_total, K'], sfa [m_total, k/32] (the
+ *   upstream gradient, quantised); b [num_groups, n, K'], sfb
+ *   [num_groups, n, k/32] (each expert's weights, K-major);
+ *   group_end [num_groups] int32 (device, cumulative ends);
+ *   c [m_total, 2n] BF16: the forward activations, alternating 32-column
+ *   blocks of the input and the gate half (input block first);
+ *   alpha, beta [num_groups] FP32 (optional: NULL means 1);
+ *   prob [m_total] FP32 routing probabilities; dprob [m_total] FP32,
+ *   accumulated (+=; zero it for a plain gradient; the adds of one row come
+ *   from several workgroups, so their FP32 order is not fixed);
+ *   d [m_total, 2n] BF16 output.
+ * n % 32 == 0, n * 1024 < 2^31; k a multiple of the tiled K step (128 MXFP8,
+ * 256 MXFP4), at least two steps; a, b, c, d 16-byte aligned; sfa, sfb, prob,
+ * dprob 4-byte aligned.  Rows at or past the last end are not written (d
+ * nor dprob).  No workspace is used.
+ */
+hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode,
+                                           const uint8_t* a, const uint8_t* sfa,
+                                           const uint8_t* b, const uint8_t* sfb,
+                                           const int32_t* group_end,
+                                           int32_t num_groups, const uint16_t* c,
+                                           const float* alpha, const float* beta,
+                                           const float* prob, float* dprob,
+                                           uint16_t* d, int64_t m_total, int64_t n,
+                                           int64_t k, int32_t cu_limit);
+
+/*
  * Grouped-masked GEMM (HALOps "GEMM" page, group_masked_gemm section): expert
  * e owns the slot of rows [e * max_m, (e + 1) * max_m); only its first
  * min(masked_m[e], max_m) rows are computed and written (padded rows are

@@ -22,6 +22,9 @@ Workloads (sizes from the pages' examples and qualification shapes):
                     counts ~ Multinomial(65536, Dirichlet(1)); each group
                     padded to a multiple of 128; K=4096, N=2*1536
   moe_masked        E=64, slot 256 rows, counts ~ U{0..256}; K=7168, N=4096
+  moe_dglu_backward the backward of the expert MLP's input at the MoE shape:
+                    moe_contiguous's routing, A [R, 4096], B [32, 1536, 4096],
+                    C [R, 3072], prob, per-expert alpha / beta
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -132,6 +135,34 @@ def moe_contiguous(seed=3, E=32, tokens=16384, topk=4, K=4096, H=1536, align=128
     if with_weights:
         out["b"] = normal_bf16_per_expert(seed * 1000 + 7, E, (2 * H, K), 0.02, threads)
     return out
+
+
+def moe_dglu_backward(seed=3, E=32, tokens=16384, topk=4, K=4096, N=1536, align=128, threads=8):
+    """Inputs of the backward grouped GEMM with the dSwiGLU epilogue at the
+    MoE shape (cuDNN FE "Grouped GEMM + dGLU (SM100)" tensors): the routing
+    of moe_contiguous (same seed: same counts and padded ends); A [R, K] the
+    upstream gradient N(0, 1) on valid rows, zero on padding rows; B
+    [E, N, K] expert weights N(0, 0.02); C [R, 2N] forward activations
+    N(0, 1); prob [R] float32 U(0, 1); alpha, beta [E] float32 U(0.5, 2) and
+    U(0.5, 1.5)."""
+    rng = np.random.default_rng(seed)
+    counts = moe_contiguous_counts(rng, E, tokens * topk)
+    ends, _ = padded_group_ends(counts, align)
+    R = int(ends[-1])
+    starts = np.concatenate([[0], ends[:-1]]).astype(np.int64)
+    r2 = np.random.default_rng([seed, 21])
+    a = np.zeros((R, K), np.uint16)
+    for g in range(E):
+        c = int(counts[g])
+        if c:
+            a[starts[g]:starts[g] + c] = normal_bf16(r2, (c, K))
+    b = normal_bf16_per_expert(seed * 1000 + 21, E, (N, K), 0.02, threads)
+    cact = normal_bf16(r2, (R, 2 * N))
+    prob = r2.random(R, dtype=np.float32)
+    alpha = r2.uniform(0.5, 2.0, E).astype(np.float32)
+    beta = r2.uniform(0.5, 1.5, E).astype(np.float32)
+    return {"counts": counts, "group_end": ends, "starts": starts, "a": a, "b": b, "c": cact, "prob": prob,
+            "alpha": alpha, "beta": beta, "K": K, "N": N}
 
 
 def moe_down_weights(E=32, hidden=4096, H=1536, seed=3, threads=8):

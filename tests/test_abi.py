@@ -198,3 +198,18 @@ def test_gemm_swiglu_rejects_offsets_past_32_bits(lib):
     h, k = 32768, 65536
     assert f(None, 0, A, A, A, A, A, 4, NUL, NUL, A, A, NUL, 1024, h, k, 0) == -2
     assert "2^31" in hq.hq_last_error()
+
+
+def test_dswiglu_rejects_before_launch(lib):
+    f = lib.hq_group_contiguous_gemm_dswiglu
+    args = lambda mode=0, n=64, k=512, c=A, prob=A, dprob=A, d=A, G=4: (
+        None, mode, A, A, A, A, A, G, c, NUL, NUL, prob, dprob, d, 64, n, k, 0)
+    assert f(*args(mode=2)) == -4              # NVFP4: not this call
+    assert f(*args(n=48)) == -2                # n % 32
+    assert f(*args(k=48)) == -2                # k % 32
+    assert f(*args(k=128)) == -2               # one MXFP8 K step
+    assert f(*args(G=0)) == -2
+    assert f(*args(c=NUL)) == -1
+    assert f(*args(dprob=NUL)) == -1
+    assert f(*args(c=MIS)) == -3
+    assert f(*args(d=MIS)) == -3
