@@ -26,9 +26,12 @@ ID runs one of them alone, e.g. under a profiler):
   n3  the backward grouped GEMM with the dSwiGLU epilogue, MXFP8, the MoE shape
       (32 experts, 65536 routed rows, K = 4096, N = 1536, C / D [rows, 3072])
   d5  quantisation bandwidth: MXFP4 [16384, 7168], NVFP4 [4096, 17408] (global
-      scale supplied, and with the amax pass)
-each with its time, achieved rate, roofline fraction and, where affordable,
-the oracle's time for the same work on the host cores.
+      scale supplied, and with the amax pass, whose bytes count the input's
+      second read: the global scale needs all of it before the first code)
+each with its time (HIP events around each launch; the launches queue behind
+a spin kernel so that short kernels are not timed with the host's launch
+latency), achieved rate, roofline fraction and, where affordable, the
+oracle's time for the same work on the host cores.
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
 of the valid rows per second), the per-kernel times, the roofline of the
@@ -401,7 +404,9 @@ def run_masked_fp4(args, torch, hq, synth):
 def _time_us(torch, fns, reps=15, per=20):
     """Median over `reps` batches of the mean time per launch of a batch of
     `per` launches (HIP events on the current stream); fns is cycled so that a
-    ring of buffers can be rotated through (cold-cache timing)."""
+    ring of buffers can be rotated through (cold-cache timing).  Each batch
+    queues behind a spin kernel (_hold_gpu), so the batch runs back to back on
+    the GPU whatever the host's time per launch."""
     i = 0
     for _ in range(10):
         fns[i % len(fns)]()
@@ -411,6 +416,7 @@ def _time_us(torch, fns, reps=15, per=20):
     for _ in range(reps):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
+        _hold_gpu(torch, 1000 + 150 * per)
         s.record()
         for _ in range(per):
             fns[i % len(fns)]()
@@ -509,13 +515,35 @@ def _oracle_threads():
         return len(os.sched_getaffinity(0))
 
 
+_SLEEP_CYCLES_PER_US = None
+
+
+def _hold_gpu(torch, us):
+    """Queues a spin kernel of about `us` microseconds on the current stream,
+    so that launches queued behind it start back to back: each event pair
+    then brackets GPU time, not the host's time to issue the next launch."""
+    global _SLEEP_CYCLES_PER_US
+    if _SLEEP_CYCLES_PER_US is None:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1 << 20)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = (1 << 20) / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US))
+
+
 def _launch_us(torch, fns, reps=30, warm=5):
     """Per-launch times (HIP events around each launch on the current stream)
     over `reps` launches after `warm` untimed ones; fns is cycled (a ring of
-    buffers for cold-cache timing).  Returns (median us, mean us)."""
+    buffers for cold-cache timing).  The launches queue behind a spin kernel
+    that outlasts their issue, so that short kernels are not timed with the
+    host's launch latency.  Returns (median us, mean us)."""
     for i in range(warm):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
+    _hold_gpu(torch, 2000 + 150 * reps)
     t = Timer(torch)
     for i in range(reps):
         t.mark("x", fns[(warm + i) % len(fns)])
@@ -749,7 +777,10 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
         bytes_ = m * kk * (2 + 0.5 + 1 / gs)
         extra = {"mean_us": round(mean, 2)}
         if mode == "nvfp4" and not supplied:
-            extra["GB/s_incl_amax_pass"] = round((bytes_ + 2 * m * kk) / (med * 1e-6) / 1e9, 1)
+            # the global scale needs the whole tensor's amax before the first
+            # code, so the input is read twice: 2 more bytes per element
+            extra["GB/s_single_read"] = round(bytes_ / (med * 1e-6) / 1e9, 1)
+            bytes_ += 2 * m * kk
         if oracle:
             rows = 256
             sample = xbits[:rows]

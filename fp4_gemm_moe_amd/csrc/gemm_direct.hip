@@ -118,7 +118,10 @@ __device__ __forceinline__ void scale_words(const uint8_t* p, bool in, uint32_t 
   }
 }
 
-template <int FMT, int FM, int FN, int NWMAX, int U, int SP = 1>
+// PA: the weights of group g sit at the addresses b_ptrs[g] / sfb_ptrs[g]
+// (discrete expert tensors) instead of at g * stride from one base; a
+// separate instantiation, so the packed-weights kernels carry no select.
+template <int FMT, int FM, int FN, int NWMAX, int U, int SP = 1, bool PA = false>
 __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
@@ -152,10 +155,8 @@ __global__ __launch_bounds__(NWMAX * 64) void mx_gemm_direct(GemmArgs p) {
       arow[fm] = p.a + r * p.lda;
       asf[fm] = p.sfa + r * p.ldsf;
     }
-    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g])
-                                 : p.b + (int64_t)tr.g * p.b_stride;
-    const uint8_t* bsg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g])
-                                    : p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* bg = PA ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g]) : p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = PA ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g]) : p.sfb + (int64_t)tr.g * p.sfb_stride;
     const uint8_t* brow[FN];
     const uint8_t* bsf[FN];
 #pragma unroll
@@ -285,8 +286,11 @@ __device__ __forceinline__ NvSlice nv_load(const uint8_t* row_codes, const uint8
 // SC16 (K % 256 == 0, scale rows 16-byte aligned): K steps in pairs as for
 // mx_gemm_direct; a lane reads the 16 scale bytes of a pair in one load and
 // decodes its two UE4M3 bytes per step with the hardware FP8 conversion.
-template <int FM, int FN, int NWMAX, int U, bool SC16 = false>
-__global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
+// PA as for mx_gemm_direct.  One-fragment tiles are held to 128 VGPRs (4
+// waves per SIMD), so that two 512-thread blocks share a CU: left alone the
+// compiler takes 129 and the skinny launch runs one block per CU.
+template <int FM, int FN, int NWMAX, int U, bool SC16 = false, bool PA = false>
+__global__ __launch_bounds__(NWMAX * 64, FM == 1 ? 4 : 1) void nv_gemm_direct(GemmArgs p) {
   constexpr int TM = 16 * FM, TN = 16 * FN;
   __shared__ TileTable tt;
   __shared__ v4f red[NWMAX - 1][FM * FN][64];
@@ -318,10 +322,8 @@ __global__ __launch_bounds__(NWMAX * 64) void nv_gemm_direct(GemmArgs p) {
       arow[fm] = p.a + r * p.lda;
       asf[fm] = p.sfa + r * p.ldsf;
     }
-    const uint8_t* bg = p.b_ptrs ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g])
-                                 : p.b + (int64_t)tr.g * p.b_stride;
-    const uint8_t* bsg = p.sfb_ptrs ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g])
-                                    : p.sfb + (int64_t)tr.g * p.sfb_stride;
+    const uint8_t* bg = PA ? reinterpret_cast<const uint8_t*>(p.b_ptrs[tr.g]) : p.b + (int64_t)tr.g * p.b_stride;
+    const uint8_t* bsg = PA ? reinterpret_cast<const uint8_t*>(p.sfb_ptrs[tr.g]) : p.sfb + (int64_t)tr.g * p.sfb_stride;
     const uint8_t* brow[FN];
     const uint8_t* bsf[FN];
 #pragma unroll
@@ -497,10 +499,9 @@ hipError_t launch_direct(hipStream_t s, K kernel, const GemmArgs& p, int TM, int
   return hipGetLastError();
 }
 
-}  // namespace
-
-// Direct path entry: picks the tile shape from the rows per group and N.
-hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+// Picks the tile shape from the rows per group and N.
+template <bool PA>
+hipError_t launch_direct_pa(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
   const int64_t rows_hint = p.form == kContiguous ? p.m_rows : p.slot_rows;
   const int fm = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
   // one 16-row fragment (skinny M): for MX the wave count follows the tile
@@ -514,14 +515,14 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
       const bool sc16 = p.k % 256 == 0 &&
                         ((reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb)) & 15) == 0;
       if (sc16) {
-        if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2, true>, p, 16, 32, dev, 1024);
-        return launch_direct(s, nv_gemm_direct<1, 2, 8, 2, true>, p, 16, 32, dev, 512);
+        if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2, true, PA>, p, 16, 32, dev, 1024);
+        return launch_direct(s, nv_gemm_direct<1, 2, 8, 2, true, PA>, p, 16, 32, dev, 512);
       }
-      if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2>, p, 16, 32, dev, 1024);
-      return launch_direct(s, nv_gemm_direct<1, 2, 8, 2>, p, 16, 32, dev, 512);
+      if (few) return launch_direct(s, nv_gemm_direct<1, 2, 16, 2, false, PA>, p, 16, 32, dev, 1024);
+      return launch_direct(s, nv_gemm_direct<1, 2, 8, 2, false, PA>, p, 16, 32, dev, 512);
     }
-    if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1>, p, 32, 32, dev);
-    return launch_direct(s, nv_gemm_direct<4, 2, 4, 1>, p, 64, 32, dev);
+    if (fm == 2) return launch_direct(s, nv_gemm_direct<2, 2, 4, 1, false, PA>, p, 32, 32, dev);
+    return launch_direct(s, nv_gemm_direct<4, 2, 4, 1, false, PA>, p, 64, 32, dev);
   }
   // scale rows in whole, aligned groups of 2 or 4 K steps (8 or 16 bytes)
   const uintptr_t sfal = reinterpret_cast<uintptr_t>(p.sfa) | reinterpret_cast<uintptr_t>(p.sfb);
@@ -530,33 +531,40 @@ hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo
   if (p.mode == kMXFP8) {
     if (fm == 1) {
       if (sc16) {
-        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 4>;
+        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 4, PA>;
         return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev, 4));
       }
       if (sc8) {
-        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 2>;
+        auto k = mx_gemm_direct<0, 1, 1, 16, 4, 2, PA>;
         return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
       }
-      auto k = mx_gemm_direct<0, 1, 1, 16, 4>;
+      auto k = mx_gemm_direct<0, 1, 1, 16, 4, 1, PA>;
       return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
     }
-    if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2, 4, 2>, p, 32, 32, dev);
-    return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2>, p, 64, 64, dev);
+    if (fm == 2) return launch_direct(s, mx_gemm_direct<0, 2, 2, 4, 2, 1, PA>, p, 32, 32, dev);
+    return launch_direct(s, mx_gemm_direct<0, 4, 4, 4, 2, 1, PA>, p, 64, 64, dev);
   }
   if (fm == 1) {
     if (sc16) {
-      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 4>;
+      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 4, PA>;
       return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev, 4));
     }
     if (sc8) {
-      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 2>;
+      auto k = mx_gemm_direct<4, 1, 1, 16, 4, 2, PA>;
       return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
     }
-    auto k = mx_gemm_direct<4, 1, 1, 16, 4>;
+    auto k = mx_gemm_direct<4, 1, 1, 16, 4, 1, PA>;
     return launch_direct(s, k, p, 16, 16, dev, 64 * skinny_waves(k, 16, p, 16, 16, dev));
   }
-  if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2, 4, 2>, p, 32, 32, dev);
-  return launch_direct(s, mx_gemm_direct<4, 4, 4, 4, 2>, p, 64, 64, dev);
+  if (fm == 2) return launch_direct(s, mx_gemm_direct<4, 2, 2, 4, 2, 1, PA>, p, 32, 32, dev);
+  return launch_direct(s, mx_gemm_direct<4, 4, 4, 4, 2, 1, PA>, p, 64, 64, dev);
+}
+
+}  // namespace
+
+// Direct path entry.
+hipError_t launch_gemm_direct(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
+  return p.b_ptrs ? launch_direct_pa<true>(s, p, dev) : launch_direct_pa<false>(s, p, dev);
 }
 
 }  // namespace hq

@@ -20,7 +20,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;       // chunks in flight per thread (quantisation)
-constexpr int kAmaxUnroll = 4;   // chunks in flight per thread (NVFP4 amax pass)
 
 struct Chunk8 {
   float f[8];
@@ -98,30 +97,26 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint4* __restr
 }
 
 // ---------------------------------------------------------------- NVFP4
-// Global scale g = amax / 2688 (FP32), computed by three tiny launches in
-// stream order: zero the accumulator, reduce |x| into it with atomicMax on the
-// bit pattern (order-preserving for non-negative floats), finalise in place.
-__global__ void nv_amax_zero(uint32_t* acc) { *acc = 0u; }
+// Global scale g = amax / 2688 (FP32), in two launches in stream order: every
+// workgroup of the first writes the |x| maximum of its block of chunks to a
+// slot of its own (the slots sit in q, whose codes are written only by the
+// quantisation that follows); one workgroup then folds the slots and writes g.
+constexpr int kAmaxUnroll = 4;   // chunks per thread (NVFP4 amax pass)
 
-// One atomic per workgroup: a wave reduction, then the first wave folds the
-// block's wave maxima.  The grid is a few workgroups per CU, each streaming
-// kAmaxUnroll independent 16-byte loads per thread per iteration of a
-// grid-stride loop (measured faster here than walking blocks of consecutive
-// chunks, which needs many more workgroups and atomics).
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restrict__ x,
                                                            int64_t nchunks,
-                                                           uint32_t* __restrict__ acc) {
+                                                           uint32_t* __restrict__ slots) {
   __shared__ uint32_t wmax[kThreads / 64];
+  constexpr int64_t kBlock = (int64_t)kAmaxUnroll * kThreads;
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < nchunks;
-       base += stride * kAmaxUnroll) {
+  for (int64_t base = (int64_t)blockIdx.x * kBlock + threadIdx.x; base < nchunks;
+       base += (int64_t)gridDim.x * kBlock) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
-      const int64_t ci = base + u * stride;
-      v[u] = ci < nchunks ? load_nt(&x[ci]) : make_uint4(0, 0, 0, 0);
+      const int64_t ci = base + u * kThreads;
+      v[u] = ci < nchunks ? x[ci] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
@@ -136,13 +131,27 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(const uint4* __restri
     uint32_t b = 0;
 #pragma unroll
     for (int i = 0; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
-    if (b != 0) atomicMax(acc, b);
+    slots[blockIdx.x] = b;
   }
 }
 
-__global__ void nv_gs_finalize(float* gs) {
-  float a = __uint_as_float(*reinterpret_cast<uint32_t*>(gs));
-  *gs = a == 0.0f ? 1.0f : a / 2688.0f;
+constexpr int kFoldThreads = 1024;
+
+__global__ __launch_bounds__(kFoldThreads) void nv_gs_fold(const uint32_t* __restrict__ slots,
+                                                           int64_t nslots, float* __restrict__ gs) {
+  __shared__ uint32_t wmax[kFoldThreads / 64];
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < nslots; i += kFoldThreads) m = slots[i] > m ? slots[i] : m;
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 0; i < kFoldThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+    const float a = __uint_as_float(b);
+    *gs = a == 0.0f ? 1.0f : a / 2688.0f;
+  }
 }
 
 // NVFP4: per 16-group (two lanes of 8), sf = UE4M3(amax_b / (6 g)),
@@ -211,14 +220,12 @@ hipError_t launch_quant_t(hipStream_t s, int mode, const uint16_t* x, int64_t m,
     hipLaunchKernelGGL((mx_quant_kernel<kMXFP4, F16>), dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf);
   } else {
     if (!gs_input) {
-      uint32_t* acc = reinterpret_cast<uint32_t*>(gs);
-      hipLaunchKernelGGL(nv_amax_zero, dim3(1), dim3(1), 0, s, acc);
-      int64_t ablocks = (nchunks + (int64_t)kThreads * kAmaxUnroll - 1) / ((int64_t)kThreads * kAmaxUnroll);
-      if (ablocks > 1024) ablocks = 1024;     // ~4 per CU: 1024 atomics at most
-      if (ablocks < 1) ablocks = 1;
-      hipLaunchKernelGGL(nv_amax_kernel<F16>, dim3((unsigned)ablocks), dim3(kThreads), 0, s, xv,
-                         nchunks, acc);
-      hipLaunchKernelGGL(nv_gs_finalize, dim3(1), dim3(1), 0, s, gs);
+      // one slot per amax workgroup, in q (4 bytes per chunk of codes)
+      const int ablocks = grid_for(nchunks, kAmaxUnroll);
+      uint32_t* slots = reinterpret_cast<uint32_t*>(q);
+      hipLaunchKernelGGL(nv_amax_kernel<F16>, dim3(ablocks), dim3(kThreads), 0, s, xv, nchunks, slots);
+      hipLaunchKernelGGL(nv_gs_fold, dim3(1), dim3(kFoldThreads), 0, s, (const uint32_t*)slots,
+                         (int64_t)ablocks, gs);
     }
     hipLaunchKernelGGL(nv_quant_kernel<F16>, dim3(grid), dim3(kThreads), 0, s, xv, nchunks, q, sf,
                        (const float*)gs);

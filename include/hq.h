@@ -102,7 +102,9 @@ const char* hq_last_error(void);
  * code = E2M1(x / (decode(sf) * g)), each division an IEEE FP32 operation
  * rounded to nearest even (code = +-0 when decode(sf) * g == 0).
  * global_scale (device float[1]) is required: read when HQ_GS_INPUT is set,
- * otherwise computed and written (the call then enqueues an amax pass).
+ * otherwise computed and written (the call then enqueues an amax pass, which
+ * uses the start of q as scratch before the codes overwrite it: x, q, sf and
+ * global_scale must not overlap).
  * Inputs convert exactly to FP32 (both formats); the rules above then apply
  * to those values.
  */
