@@ -103,6 +103,7 @@ __device__ __forceinline__ v16f mfma32(v8i w, v8i x, v16f acc, int sw, int sx) {
 }
 
 constexpr int BM = 256, BN = 256;
+constexpr int kMB = 8;                      // m-tiles per block of the tile order (make_tile)
 constexpr int SROW = 128;                   // bytes of a row per stage
 constexpr int kNV = 2;                      // format tag of the NVFP4 instantiation
 
@@ -243,14 +244,15 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
     slice = t / per_slice;
     t -= slice * per_slice;
   }
-  // blocks of 4 m-tiles x all n-tiles, walked n-major inside the block so 32
-  // consecutive tiles = 4 m x 8 n
-  const int blk = t / (4 * NT);
-  const int rem = t - blk * 4 * NT;
-  const int mrem = total_gm - blk * 4;
-  const int mb = mrem < 4 ? mrem : 4;
+  // blocks of 8 m-tiles x all n-tiles, walked n-major inside the block so 32
+  // consecutive tiles (one XCD's share of a round) = 8 m x 4 n (measured 2 %
+  // faster on the grouped MXFP8 GEMMs than blocks of 4 m-tiles)
+  const int blk = t / (kMB * NT);
+  const int rem = t - blk * kMB * NT;
+  const int mrem = total_gm - blk * kMB;
+  const int mb = mrem < kMB ? mrem : kMB;
   const int nt = rem / mb;
-  const int gm = blk * 4 + (rem - nt * mb);
+  const int gm = blk * kMB + (rem - nt * mb);
   int g;
   int64_t row0, row_end;
   if (p.form == kUniform) {
@@ -1165,8 +1167,8 @@ SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
   const int64_t kTailMinSteps = p.mode == kNVFP4 ? 12 : (p.mode == kMXFP8 ? 48 : 40);
   if (p.num_groups == 1 && tiles > grid_full && nk >= kTailMinSteps) {
     const int64_t tail = tiles % grid_full;
-    const int64_t last_blk = (total_gm - 1) / 4;
-    const int64_t mb = total_gm - last_blk * 4;           // m-tiles of the last block
+    const int64_t last_blk = (total_gm - 1) / kMB;
+    const int64_t mb = total_gm - last_blk * kMB;         // m-tiles of the last block
     const int64_t cols = (tail + mb - 1) / mb;            // n-tile columns of the rectangle
     int64_t S = cols * mb > 0 ? grid_full / (cols * mb) : 0;
     if (S > nk / 4) S = nk / 4;
@@ -1174,7 +1176,7 @@ SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
     if (tail > 0 && tail * 2 <= grid_full && cols < NT && S >= 2) {
       sp.kind = kSplitTail;
       sp.S = S;
-      sp.r0 = last_blk * 4 * BM;
+      sp.r0 = last_blk * kMB * BM;
       sp.c0 = (NT - cols) * BN;
       sp.rect_tiles = cols * mb;
       sp.bytes = (uint64_t)(S * (p.m_rows - sp.r0) * (p.n - sp.c0) * 4);
