@@ -28,9 +28,9 @@ ID runs one of them alone, e.g. under a profiler):
   d5  quantisation bandwidth: MXFP4 [16384, 7168], NVFP4 [4096, 17408] (global
       scale supplied, and with the amax pass, whose bytes count the input's
       second read: the global scale needs all of it before the first code)
-each with its time (HIP events around each launch; the launches queue behind
-a spin kernel so that short kernels are not timed with the host's launch
-latency), achieved rate, roofline fraction and, where affordable, the
+each with its time per launch (HIP events around batches of back-to-back
+launches queued behind a spin kernel, so that short kernels are timed
+without the host's launch latency or per-launch event markers), achieved rate, roofline fraction and, where affordable, the
 oracle's time for the same work on the host cores.
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
@@ -42,6 +42,8 @@ the oracle timed on a bounded sample on the host cores, and the configs.
                     [--workload moe|moe_unfused|moe_mlp|dense_fp4|masked_fp4|permute|configs]
     python bench.py --workload sweep    # dense qualification grid + quant bandwidths,
                                         # one JSON line per case
+    python bench.py --workload ab --ab-lib OTHER/libhq.so   # interleaved A/B of the
+                                        # skinny cells and NVFP4 quant against another build
 """
 import argparse
 import json
@@ -534,22 +536,35 @@ def _hold_gpu(torch, us):
     torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US))
 
 
-def _launch_us(torch, fns, reps=30, warm=5):
-    """Per-launch times (HIP events around each launch on the current stream)
-    over `reps` launches after `warm` untimed ones; fns is cycled (a ring of
-    buffers for cold-cache timing).  The launches queue behind a spin kernel
-    that outlasts their issue, so that short kernels are not timed with the
-    host's launch latency.  Returns (median us, mean us)."""
+def _launch_us(torch, fns, reps=30, warm=5, per=None):
+    """Time per launch: HIP events on the current stream around batches of
+    `per` back-to-back launches (about reps launches in all, at least 5
+    batches) after `warm` untimed ones; fns is cycled (a ring of buffers for
+    cold-cache timing).  Each batch queues behind a spin kernel that outlasts
+    its issue, so the launches run back to back whatever the host's time per
+    launch, and no event marker sits between two launches (a marker pair
+    around every launch adds about 5 us).  Returns (median, mean) over the
+    batches of the mean time per launch, in us."""
     for i in range(warm):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
-    _hold_gpu(torch, 2000 + 150 * reps)
-    t = Timer(torch)
-    for i in range(reps):
-        t.mark("x", fns[(warm + i) % len(fns)])
-    torch.cuda.synchronize()
-    v = np.array(t.times_ms("x")) * 1e3
-    return float(np.median(v)), float(np.mean(v))
+    if per is None:
+        per = max(1, reps // 5)
+    nb = max(5, reps // per)
+    res = []
+    i = warm
+    for _ in range(nb):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        _hold_gpu(torch, 1000 + 150 * per)
+        s.record()
+        for _ in range(per):
+            fns[i % len(fns)]()
+            i += 1
+        e.record()
+        torch.cuda.synchronize()
+        res.append(s.elapsed_time(e) * 1e3 / per)
+    return float(np.median(res)), float(np.mean(res))
 
 
 def _oracle_us(fn, reps=3):
@@ -562,8 +577,10 @@ def _oracle_us(fn, reps=3):
 
 
 def _rec(cid, workload, us, flops=None, bytes_=None, bound="mfma", peak_key="mxfp8", **extra):
-    """One config record: time, achieved rate against the bound's peak."""
-    r = {"id": cid, "workload": workload, "us": round(us, 2)}
+    """One config record: time, achieved rate against the bound's peak, and
+    the call's HBM bytes measured by counters (profiles/traffic.json, key =
+    the config id; None when unmeasured or the sources changed since)."""
+    r = {"id": cid, "workload": workload, "us": round(us, 2), "traffic": _traffic(cid)}
     if flops is not None:
         r["TFLOP/s"] = round(flops / (us * 1e-6) / 1e12, 2)
     if bytes_ is not None:
@@ -797,13 +814,98 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
     return recs
 
 
+def run_ab(args, torch, hq, synth):
+    """Interleaved A/B of this build against another build of libhq.so
+    (--ab-lib PATH, e.g. built from an earlier commit in a git worktree):
+    the skinny dense cells (raw hq_dense_gemm, whose C signature both builds
+    share) and NVFP4 quantisation with the amax pass.  Inputs are quantised
+    by this build; per case the two builds alternate batch by batch (each
+    batch queued behind a spin kernel), and their outputs are compared
+    bit for bit.  One JSON line per case."""
+    import ctypes
+    other = ctypes.CDLL(os.path.abspath(args.ab_lib))
+    for name in ("hq_dense_gemm", "hq_group_wise_quant"):
+        a, r = hq._SIGS[name]
+        f = getattr(other, name)
+        f.argtypes, f.restype = a, r
+    libs = {"this": hq.load(), "other": other}
+    dev = torch.device("cuda:0")
+
+    def ab(label, call, outs, work, unit, reps=12, per=20):
+        ref = None
+        same = True
+        for nm in ("this", "other"):
+            for o in outs:
+                o.view(torch.uint8).fill_(0xA5)
+            call(libs[nm])
+            torch.cuda.synchronize()
+            got = [o.clone() for o in outs]
+            if ref is None:
+                ref = got
+            else:
+                same = all(torch.equal(x.view(torch.uint8), y.view(torch.uint8)) for x, y in zip(ref, got))
+        res = {"this": [], "other": []}
+        for nm in ("this", "other"):
+            for _ in range(3):
+                call(libs[nm])
+        torch.cuda.synchronize()
+        for r in range(reps):
+            for nm in (("this", "other") if r % 2 == 0 else ("other", "this")):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                _hold_gpu(torch, 1000 + 150 * per)
+                e0.record()
+                for _ in range(per):
+                    call(libs[nm])
+                e1.record()
+                torch.cuda.synchronize()
+                res[nm].append(e0.elapsed_time(e1) * 1e3 / per)
+        ut, uo = float(np.median(res["this"])), float(np.median(res["other"]))
+        line = {"workload": label, "us_this": round(ut, 2), "us_other": round(uo, 2),
+                "this_over_other": round(ut / uo, 3), "same_bits": bool(same),
+                unit: round(work / (ut * 1e-6) / 1e9, 1), "other_lib": args.ab_lib}
+        print(json.dumps(line), flush=True)
+
+    for mode in ("nvfp4", "mxfp4"):
+        for n, k, m in ((17408, 5120, 1), (12288, 5120, 16), (5120, 17408, 1)):
+            w = _dev_bf16(torch, synth.dense_fp4_large_weights(n, k), dev)
+            x = _dev_bf16(torch, synth.dense_fp4_large_acts(n, k, m), dev)
+            wq, wsf, gw = hq.quantize(w, mode)
+            aq, asf, ga = hq.quantize(x, mode)
+            al = (ga * gw) if mode == "nvfp4" else None
+            out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            st = hq._stream(aq)
+            ptr = [hq._p(t) for t in (aq, asf, wq, wsf)]
+            pal, po = hq._p(al), hq._p(out)
+
+            def call(L, mc=hq.MODES[mode], st=st, ptr=ptr, pal=pal, po=po, m=m, n=n, k=k):
+                rc = L.hq_dense_gemm(st, mc, ptr[0], ptr[1], ptr[2], ptr[3], None, pal, po, m, n, k, 0)
+                if rc != 0:
+                    raise RuntimeError(f"hq_dense_gemm returned {rc}")
+            gs = 16 if mode == "nvfp4" else 32
+            ab(f"dense_{mode}_M{m}_N{n}_K{k}_warm", call, [out], (m + n) * k * (0.5 + 1 / gs) + 2 * m * n, "GB/s")
+            del w, x, wq, wsf, aq, asf, out
+    m, k = 4096, 17408
+    x = _dev_bf16(torch, synth.normal_bf16(np.random.default_rng(5), (m, k)), dev)
+    q = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    sf = torch.empty(m, k // 16, dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    st = hq._stream(x)
+    px, pq, psf, pg = hq._p(x), hq._p(q), hq._p(sf), hq._p(g)
+
+    def callq(L):
+        rc = L.hq_group_wise_quant(st, hq.HQ_NVFP4, px, m, k, pq, psf, pg, 0)
+        if rc != 0:
+            raise RuntimeError(f"hq_group_wise_quant returned {rc}")
+    ab(f"quant_nvfp4_{m}x{k}_amax_warm", callq, [q, sf, g], m * k * (2 + 2 + 0.5 + 1 / 16), "GB/s_incl_second_read")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe", choices=["moe", "moe_unfused", "moe_mlp", "dense_fp4",
-                                                       "masked_fp4", "permute", "sweep", "configs"])
+                                                       "masked_fp4", "permute", "sweep", "configs", "ab"])
     ap.add_argument("--mode", default="mxfp4")
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=17408)
@@ -812,6 +914,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config records")
     ap.add_argument("--only", default=None, help="run one config record alone (--workload configs)")
+    ap.add_argument("--ab-lib", default=None, help="--workload ab: another build of libhq.so to time against")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -842,6 +945,11 @@ def main():
         del src, dst
     if args.workload == "sweep":
         run_sweep(args, torch, hq, synth)
+        return
+    if args.workload == "ab":
+        if not args.ab_lib:
+            raise SystemExit("--workload ab needs --ab-lib PATH (another build of libhq.so)")
+        run_ab(args, torch, hq, synth)
         return
     if args.workload == "configs":
         recs = run_configs(torch, hq, synth, only=args.only, oracle=not args.no_cpu_baseline)
