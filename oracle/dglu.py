@@ -35,12 +35,20 @@ Readings (the page leaves these open or states them twice):
      (the page's caller-zeroed dprob).
   5. D is BF16 (the page's default d_dtype), rounded once from the exact
      value.
+  6. Row-quantised D (the page's optional output quantisation, "Step 3"):
+     each row's 32-column groups of the BF16 D -- one input or gate block
+     each -- take the MXFP8 rule of group_wise_quant (UE8M0 scale per 32,
+     E4M3 codes).  The page's own FP8 recipe (a norm_const times the block
+     amax times a reciprocal maximum, with 128x4 scale atoms) is not the
+     OCP MX rule the rest of the library follows; the library's rule on the
+     BF16 values is the reading taken, so the codes equal group_wise_quant
+     applied to the BF16 D output.
 """
 
 import numpy as np
 
 from . import formats as F
-from .quant import dequant
+from .quant import dequant, mx_quant_bf16
 
 BLOCK = 32
 
@@ -148,3 +156,21 @@ def d_tolerance(mode, a, sfa, b, sfb, group_end, c_bits, prob, alpha=None, beta=
         tD[lo:hi, gc] = slack * pr * np.abs(inp * sig * (1.0 + gate * (1.0 - sig)))
         tP[lo:hi] = np.sum(slack * np.abs(swish * inp), axis=1)
     return tD, tP
+
+
+def grouped_gemm_dswiglu_quant(mode, a, sfa, b, sfb, group_end, c_bits, prob, alpha=None, beta=None,
+                               dprob_in=None, q_out=None, sf_out=None):
+    """Row-quantised D (reading 6): MXFP8 codes [M, 2N] u8 and UE8M0 scales
+    [M, 2N / 32] u8 of the BF16 D of grouped_gemm_dswiglu, on the written
+    rows (others keep ``q_out`` / ``sf_out``, zeros when None); float64
+    dprob [M]; the written-row mask."""
+    D, dprob, written = grouped_gemm_dswiglu(mode, a, sfa, b, sfb, group_end, c_bits, prob, alpha, beta,
+                                             dprob_in)
+    M, N2 = D.shape
+    q = np.zeros((M, N2), np.uint8) if q_out is None else np.array(q_out, dtype=np.uint8, copy=True)
+    sf = np.zeros((M, N2 // BLOCK), np.uint8) if sf_out is None else np.array(sf_out, dtype=np.uint8, copy=True)
+    if written.any():
+        qw, sw = mx_quant_bf16(D[written], "mxfp8")
+        q[written] = qw
+        sf[written] = sw
+    return q, sf, dprob, written

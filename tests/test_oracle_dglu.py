@@ -225,3 +225,64 @@ def test_tolerance_hand_worked():
     np.testing.assert_allclose(tD[1, :32], 1.5e-3 * 2.0 * 2.0 * s, rtol=1e-12)
     np.testing.assert_allclose(tD[1, 32:], 1.5e-3 * 2.0 * s * (1.0 + 2.0 * (1.0 - s)), rtol=1e-12)
     np.testing.assert_allclose(tP[1], 32 * 1.5e-3 * 2.0 * s, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- row-quantised D
+def test_quantised_d_hand_worked_block():
+    """One row, N = 32: gate = 0 and input = 2 give d_input = 0 and
+    d_gate = R * prob * 2 * 1/2 * (1 + 0) = R exactly (prob = 1), with
+    R[n] = n + 1 from integer codes (A = [1, 1, 0, ...], B[n] = [x_n, y_n, 0, ...],
+    x_n + y_n = n + 1).  The gate block's amax 32 gives the UE8M0 byte
+    127 + 5 - 8 = 124 (scale 2^-3), so its codes are E4M3 of 8 (n + 1),
+    worked out by hand: 8 -> 0x50, 16 -> 0x58, 24 -> 0x5C, 72 = 64 * 1.125 ->
+    0x69, 136 (midway 128 / 144) -> 128 = 0x70, 152 (midway 144 / 160) -> 160 =
+    0x72, 200 (midway 192 / 208) -> 192 = 0x74, 256 -> 0x78.  The all-zero
+    input block takes byte 0 and +0 codes."""
+    N, K = 32, 64
+    rv = np.arange(1, N + 1)
+    x = np.minimum(rv, 16)
+    y = rv - x
+    bv = np.zeros((1, N, K), np.int64)
+    bv[0, :, 0], bv[0, :, 1] = x, y
+    av = np.zeros((1, K), np.int64)
+    av[0, :2] = 1
+    a = _int_codes(av, "mxfp8")
+    b = _int_codes(bv.reshape(N, K), "mxfp8").reshape(1, N, K)
+    sfa = np.full((1, K // 32), 127, np.uint8)
+    sfb = np.full((1, N, K // 32), 127, np.uint8)
+    c = np.zeros((1, 2 * N), np.uint16)
+    c[0, :N] = 0x4000                                   # input block: 2.0; gate block: +0
+    q, sf, dp, written = DG.grouped_gemm_dswiglu_quant("mxfp8", a, sfa, b, sfb, np.array([1], np.int32), c,
+                                                        np.ones(1, np.float32))
+    assert written.all() and dp[0] == 0.0
+    assert list(sf[0]) == [0, 124]
+    assert np.all(q[0, :N] == 0)
+    want = {1: 0x50, 2: 0x58, 3: 0x5C, 9: 0x69, 17: 0x70, 19: 0x72, 25: 0x74, 32: 0x78}
+    for r, code in want.items():
+        assert q[0, N + r - 1] == code, (r, hex(q[0, N + r - 1]))
+
+
+def test_quantised_d_within_half_an_e4m3_step_and_untouched_rows():
+    """Random case: every code times its scale is within half an E4M3 step
+    of the BF16 D (relative 2^-4 for normal codes, 2^-10 absolute times the
+    scale below 2^-6, 448 times the scale when saturated), and rows past the
+    last end keep the caller's bytes."""
+    cs = _case("mxfp8", seed=7)
+    Dbits, _, written = DG.grouped_gemm_dswiglu(cs["mode"], cs["a"], cs["sfa"], cs["b"], cs["sfb"], cs["ends"],
+                                                cs["c"], cs["prob"], cs["alpha"], cs["beta"])
+    M, N2 = Dbits.shape
+    q0 = np.full((M, N2), 0xA5, np.uint8)
+    s0 = np.full((M, N2 // 32), 0x5A, np.uint8)
+    q, sf, _, w2 = DG.grouped_gemm_dswiglu_quant(cs["mode"], cs["a"], cs["sfa"], cs["b"], cs["sfb"], cs["ends"],
+                                                 cs["c"], cs["prob"], cs["alpha"], cs["beta"], q_out=q0, sf_out=s0)
+    assert np.array_equal(w2, written)
+    assert np.all(q[~written] == 0xA5) and np.all(sf[~written] == 0x5A)
+    D = F.bf16_decode(Dbits[written])
+    scale = np.exp2(sf[written].astype(np.float64) - 127).repeat(32, axis=1)
+    deq = F.e4m3_decode(q[written]) * scale
+    v = np.abs(D) / scale
+    tol = np.where(v >= 2.0 ** -6, 2.0 ** -4 * np.abs(D), 2.0 ** -10 * scale)
+    sat = v > 448
+    assert np.all(np.abs(deq - D)[~sat] <= tol[~sat] * (1 + 1e-12))
+    assert np.all(np.abs(deq[sat]) == 448 * scale[sat])
+    assert np.all(np.sign(deq)[D != 0] == np.sign(D)[D != 0])
