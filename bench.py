@@ -24,7 +24,8 @@ ID runs one of them alone, e.g. under a profiler):
       workspace: K split at M = 512, tail split at 4096)
   d4  grouped-masked MXFP4, 64 experts x 256-row slots, K = 7168, N = 4096
   n3  the backward grouped GEMM with the dSwiGLU epilogue, MXFP8, the MoE shape
-      (32 experts, 65536 routed rows, K = 4096, N = 1536, C / D [rows, 3072])
+      (32 experts, 65536 routed rows, K = 4096, N = 1536, C / D [rows, 3072]);
+      n3_q the same with D row-quantised (MXFP8 codes + UE8M0 scales)
   d5  quantisation bandwidth: MXFP4 [16384, 7168], NVFP4 [4096, 17408] (global
       scale supplied, and with the amax pass, whose bytes count the input's
       second read: the global scale needs all of it before the first code)
@@ -597,7 +598,7 @@ def _rec(cid, workload, us, flops=None, bytes_=None, bound="mfma", peak_key="mxf
 CONFIG_IDS = ["d0", "d1_batch", "d1_batch_bias", "d1_mxfp4",
               "d2_mxfp4_M1", "d2_mxfp4_M512", "d2_mxfp4_M4096",
               "d2_nvfp4_M1", "d2_nvfp4_M512", "d2_nvfp4_M4096",
-              "d4", "n3", "d5_mxfp4", "d5_nvfp4", "d5_nvfp4_amax"]
+              "d4", "n3", "n3_q", "d5_mxfp4", "d5_nvfp4", "d5_nvfp4_amax"]
 
 
 def run_configs(torch, hq, synth, only=None, oracle=True):
@@ -744,7 +745,7 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
         torch.cuda.empty_cache()
 
     # n3: the backward grouped GEMM with the dSwiGLU epilogue at the MoE shape
-    if want("n3"):
+    if want("n3") or want("n3_q"):
         d = synth.moe_dglu_backward(threads=16)
         counts, ends = d["counts"], d["group_end"]
         R, K, N, E = int(ends[-1]), d["K"], d["N"], len(counts)
@@ -760,16 +761,28 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
         al, be = torch.from_numpy(d["alpha"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
         dprob = torch.zeros(R, dtype=torch.float32, device=dev)
         dout = torch.empty(R, 2 * N, dtype=torch.bfloat16, device=dev)
-        med, mean = _launch_us(torch, [lambda: hq.hq_group_contiguous_gemm_dswiglu(
-            "mxfp8", qa, sa, qw, sw, ge, c, prob, dprob, dout, alpha=al, beta=be)], reps=20)
         flops = 2.0 * T * N * K
         # A codes + scales and C, D of the valid rows, the experts' weights, prob and dprob
         bytes_ = T * K * (1 + 1 / 32) + E * N * K * (1 + 1 / 32) + 2 * T * 2 * N * 2 + 12 * T
-        t_ideal = max(flops / (PEAK_TFLOPS["mxfp8"] * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9))
-        emit(_rec("n3", "moe_bwd_dswiglu_mxfp8_E32_T65536_K4096_N1536", med, flops=flops, bytes_=bytes_,
-                  bound="mfma", mean_us=round(mean, 2), routed_rows=T,
-                  hbm_frac=round(bytes_ / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
-                  roofline_frac=round(t_ideal / (med * 1e-6), 3)))
+        if want("n3"):
+            med, mean = _launch_us(torch, [lambda: hq.hq_group_contiguous_gemm_dswiglu(
+                "mxfp8", qa, sa, qw, sw, ge, c, prob, dprob, dout, alpha=al, beta=be)], reps=20)
+            t_ideal = max(flops / (PEAK_TFLOPS["mxfp8"] * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9))
+            emit(_rec("n3", "moe_bwd_dswiglu_mxfp8_E32_T65536_K4096_N1536", med, flops=flops, bytes_=bytes_,
+                      bound="mfma", mean_us=round(mean, 2), routed_rows=T,
+                      hbm_frac=round(bytes_ / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
+                      roofline_frac=round(t_ideal / (med * 1e-6), 3)))
+        if want("n3_q"):
+            # the same with D written row-quantised (MXFP8 codes + UE8M0 per 32)
+            dq = torch.empty(R, 2 * N, dtype=torch.uint8, device=dev)
+            dsf = torch.empty(R, 2 * N // 32, dtype=torch.uint8, device=dev)
+            med, mean = _launch_us(torch, [lambda: hq.hq_group_contiguous_gemm_dswiglu_quant(
+                "mxfp8", qa, sa, qw, sw, ge, c, prob, dprob, dq, dsf, alpha=al, beta=be)], reps=20)
+            bq = bytes_ - T * 2 * N * (2 - 1 - 1 / 32)
+            emit(_rec("n3_q", "moe_bwd_dswiglu_mxfp8_E32_T65536_K4096_N1536_rowquant_d", med, flops=flops,
+                      bytes_=bq, bound="mfma", mean_us=round(mean, 2), routed_rows=T,
+                      hbm_frac=round(bq / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)))
+            del dq, dsf
         del qa, qw, c, dout, dprob, d
         torch.cuda.empty_cache()
 

@@ -21,7 +21,7 @@ __all__ = [
     "gemm_workspace", "ptr_arrays", "hq_dense_gemm_scratch", "HQ_SCRATCH_BYTES",
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
-    "hq_group_contiguous_gemm_dswiglu",
+    "hq_group_contiguous_gemm_dswiglu", "hq_group_contiguous_gemm_dswiglu_quant",
     "hq_prefill_permute_to_masked_gemm", "prefill_permute_to_masked_gemm",
     "HQ_SCALE_BROADCAST", "HQ_SCALE_DIRECT",
     "hq_last_error", "library_path", "load", "EXPORTED_SYMBOLS",
@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "hq_group_contiguous_gemm", "hq_group_masked_gemm", "hq_fused_swiglu_quant",
     "hq_group_contiguous_gemm_swiglu_quant", "hq_group_contiguous_gemm_ptr_array",
     "hq_prefill_permute_to_masked_gemm", "hq_group_contiguous_gemm_dswiglu",
+    "hq_group_contiguous_gemm_dswiglu_quant",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,8 @@ _SIGS = {
                                                _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_group_contiguous_gemm_dswiglu": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
                                           _VP, _I64, _I64, _I64, _I32], _I32),
+    "hq_group_contiguous_gemm_dswiglu_quant": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP,
+                                                _VP, _VP, _VP, _I64, _I64, _I64, _I32], _I32),
     "hq_group_masked_gemm": ([_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _VP, _VP, _VP,
                               _I64, _I64, _I32], _I32),
     "hq_fused_swiglu_quant": ([_VP, _I32, _VP, _I64, _I64, _I32, _VP, _I64, _VP, _VP, _VP,
@@ -385,6 +388,32 @@ def hq_group_contiguous_gemm_dswiglu(mode, a, sfa, b, sfb, group_end, c, prob, d
     _check(load().hq_group_contiguous_gemm_dswiglu(
         _stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(group_end), E, _p(c), _p(alpha), _p(beta),
         _p(prob), _p(dprob), _p(d), rows, n, k, cu_limit))
+
+
+def hq_group_contiguous_gemm_dswiglu_quant(mode, a, sfa, b, sfb, group_end, c, prob, dprob, dq, dsf,
+                                           alpha=None, beta=None, cu_limit=0):
+    """hq_group_contiguous_gemm_dswiglu with D written row-quantised: dq
+    [rows, 2n] uint8 E4M3 codes and dsf [rows, 2n/32] uint8 UE8M0 scales (the
+    MXFP8 rule of hq_group_wise_quant on the BF16 D)."""
+    mode = _mode(mode)
+    rows, kc = a.shape
+    E, n, _ = b.shape
+    k = kc * (1 if mode == HQ_MXFP8 else 2)
+    _need(a, "a", torch.uint8, rows * code_cols(mode, k))
+    _need(sfa, "sfa", torch.uint8, rows * (k // group_size(mode)))
+    _need(b, "b", torch.uint8, E * n * code_cols(mode, k))
+    _need(sfb, "sfb", torch.uint8, E * n * (k // group_size(mode)))
+    _need(group_end, "group_end", torch.int32, E)
+    _need(c, "c", torch.bfloat16, rows * 2 * n)
+    _need(prob, "prob", torch.float32, rows)
+    _need(dprob, "dprob", torch.float32, rows)
+    _need(dq, "dq", torch.uint8, rows * 2 * n)
+    _need(dsf, "dsf", torch.uint8, rows * 2 * n // 32)
+    _need(alpha, "alpha", torch.float32, E)
+    _need(beta, "beta", torch.float32, E)
+    _check(load().hq_group_contiguous_gemm_dswiglu_quant(
+        _stream(a), mode, _p(a), _p(sfa), _p(b), _p(sfb), _p(group_end), E, _p(c), _p(alpha), _p(beta),
+        _p(prob), _p(dprob), _p(dq), _p(dsf), rows, n, k, cu_limit))
 
 
 def hq_group_masked_gemm(mode, a, sfa, b, sfb, masked_m, out, max_m, bias=None, alpha=None,

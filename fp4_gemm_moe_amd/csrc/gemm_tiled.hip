@@ -461,7 +461,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // scales of y instead of the gate|up output; kEpiDswiglu (the backward
 // GEMM, grouped-contiguous) applies the dSwiGLU derivative to R with the
 // forward activations C and writes D and the dprob row sums.
-constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4;
+constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4, kEpiDswigluQ = 5;
 
 template <int FMT, int EPI, bool GS>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
@@ -472,8 +472,9 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // on no fewer being issued after the next tile's loads)
   // (kEpiDswiglu issues FI * FJ * 4 stores after its loads of C; a smaller
   // count only makes the waits stricter, and vmcnt holds at most 63)
-  constexpr int kStores = EPI == kEpiSwiglu ? FI * 2 * 3 : (EPI == kEpiDswiglu ? 32 : C::kStores);
-  static_assert(EPI != kEpiDswiglu || FI * FJ * 4 >= 32, "the dSwiGLU epilogue issues at least 32 stores");
+  constexpr bool DSW = EPI == kEpiDswiglu || EPI == kEpiDswigluQ;
+  constexpr int kStores = EPI == kEpiSwiglu ? FI * 2 * 3 : (DSW ? 32 : C::kStores);
+  static_assert(!DSW || FI * FJ * 4 >= 32, "the dSwiGLU epilogues issue at least 32 stores");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TiledTable tt;
 
@@ -812,7 +813,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
             __builtin_amdgcn_raw_buffer_store_b128(o, prsrc, (int)off, 0, 0);
           }
         }
-    } else if constexpr (EPI == kEpiDswiglu) {
+    } else if constexpr (DSW) {
       // ---- dSwiGLU epilogue (cuDNN FE "Grouped GEMM + dGLU (SM100)", Step 2,
       // dSwiGLU).  Fragment (i, j) of this wave holds R columns
       // nb = n0 + wn WTN + 32 j + [0, 32) -- one 32-column block pair of C and D,
@@ -834,9 +835,18 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(uniform_ptr(reinterpret_cast<const uint8_t*>(p.c_in + tl.row0 * C2))), (short)0,
           (int)cbytes, 0x00020000);
+      // BF16 D, or (kEpiDswigluQ) its MXFP8 codes [rows, 2n] and UE8M0
+      // scales [rows, 2n / 32]: per row, each 32-column block of D (one input
+      // or gate block) is one scale group, quantised from the BF16 values
+      // with the rule of hq_group_wise_quant
       const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(uniform_ptr(reinterpret_cast<const uint8_t*>(p.d_out + tl.row0 * C2))), (short)0,
-          (int)cbytes, 0x00020000);
+          const_cast<uint8_t*>(uniform_ptr(EPI == kEpiDswigluQ
+                                               ? p.q_out + tl.row0 * C2
+                                               : reinterpret_cast<const uint8_t*>(p.d_out + tl.row0 * C2))),
+          (short)0, (int)(EPI == kEpiDswigluQ ? cbytes / 2 : cbytes), 0x00020000);
+      const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(uniform_ptr(EPI == kEpiDswigluQ ? p.sf_out + tl.row0 * (C2 / 32) : p.sf_out)),
+          (short)0, (int)(EPI == kEpiDswigluQ ? cbytes / 64 : 0), 0x00020000);
       const float al = p.alpha != nullptr ? p.alpha[tl.g] : 1.0f;
       const float a2 = al * al;
       const float be = p.beta != nullptr ? p.beta[tl.g] : 1.0f;
@@ -851,11 +861,12 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
         const int64_t mr = wm * WTM + i * 32 + re;             // row within the tile
         const bool row_ok = mr < trows;
         const float pr = row_ok ? p.prob[tl.row0 + mr] : 0.0f;
-        // the C runs of every fragment of the row: input and gate, 16 bytes each
+        // the C runs of every fragment of the row: input and gate, 16 bytes
+        // each (the quantising epilogue loads them fragment by fragment: its
+        // codes and scales need more registers)
         v4u cin[FJ][2], cgt[FJ][2];
         uint32_t coff[FJ][2];
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) {
+        auto load_c = [&](int j) {
           const int64_t nb = tl.n0 + wn * WTN + j * 32;        // first R column of the pair
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
@@ -864,10 +875,16 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
             cin[j][e] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)coff[j][e], 0, 0);
             cgt[j][e] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(coff[j][e] + 64u), 0, 0);
           }
+        };
+        if constexpr (EPI == kEpiDswiglu) {
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) load_c(j);
         }
         float dsum = 0.0f;
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
+          if constexpr (EPI == kEpiDswigluQ) load_c(j);
+          uint32_t din[2][4], dgt[2][4];       // BF16 pairs of the lane's two runs
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             float run[8];
@@ -878,7 +895,6 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
               run[r] = __uint_as_float(sw[0]);
               run[4 + r] = __uint_as_float(sw[1]);
             }
-            uint32_t din[4], dgt[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               float dv[2], gv[2];
@@ -896,12 +912,60 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
                 gv[u] = rp * xi * sg * (1.0f + xg * (1.0f - sg));
                 dsum += coff[j][e] != 0x80000000u ? swish * xi * r : 0.0f;
               }
-              din[q] = pack_bf16x2(dv[0], dv[1]);
-              dgt[q] = pack_bf16x2(gv[0], gv[1]);
+              din[e][q] = pack_bf16x2(dv[0], dv[1]);
+              dgt[e][q] = pack_bf16x2(gv[0], gv[1]);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(v4u{din[0], din[1], din[2], din[3]}, drs, (int)coff[j][e], 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(v4u{dgt[0], dgt[1], dgt[2], dgt[3]}, drs,
-                                                   (int)(coff[j][e] + 64u), 0, 0);
+            if constexpr (EPI == kEpiDswiglu) {
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{din[e][0], din[e][1], din[e][2], din[e][3]}, drs,
+                                                     (int)coff[j][e], 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(v4u{dgt[e][0], dgt[e][1], dgt[e][2], dgt[e][3]}, drs,
+                                                     (int)(coff[j][e] + 64u), 0, 0);
+            }
+          }
+          if constexpr (EPI == kEpiDswigluQ) {
+            // the block's amax over this lane's two runs and lane l ^ 32's,
+            // on the BF16 bit patterns (|x| of the upper half is bits & 0x7fff0000)
+            uint32_t ai = 0, ag = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t i0 = (din[e][q] << 16) & 0x7fffffffu, i1 = din[e][q] & 0x7fff0000u;
+                const uint32_t g0 = (dgt[e][q] << 16) & 0x7fffffffu, g1 = dgt[e][q] & 0x7fff0000u;
+                ai = i0 > ai ? i0 : ai;
+                ai = i1 > ai ? i1 : ai;
+                ag = g0 > ag ? g0 : ag;
+                ag = g1 > ag ? g1 : ag;
+              }
+            const uint32_t oi = (uint32_t)__shfl_xor((int)ai, 32, 64);
+            const uint32_t og = (uint32_t)__shfl_xor((int)ag, 32, 64);
+            ai = oi > ai ? oi : ai;
+            ag = og > ag ? og : ag;
+            const uint32_t sbi = mx_scale_byte<8>(ai), sbg = mx_scale_byte<8>(ag);
+            typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float vi[8], vg[8];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                vi[2 * q] = bf16_lo(din[e][q]);
+                vi[2 * q + 1] = bf16_hi(din[e][q]);
+                vg[2 * q] = bf16_lo(dgt[e][q]);
+                vg[2 * q + 1] = bf16_hi(dgt[e][q]);
+              }
+              // code bytes sit at half the BF16 byte offset (drop marker kept)
+              const uint32_t qo = coff[j][e] == 0x80000000u ? 0x80000000u : coff[j][e] / 2;
+              const uint2 ci = mx_fp8x8(vi, sbi), cg = mx_fp8x8(vg, sbg);
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{ci.x, ci.y}, drs, (int)qo, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(v2u{cg.x, cg.y}, drs, (int)(qo + 32u), 0, 0);
+            }
+            // scale bytes of the input and gate blocks from lane group 0 (the
+            // other group's stores take the drop marker)
+            const int64_t nb = tl.n0 + wn * WTN + j * 32;
+            const uint32_t so = he == 0 && nb < p.n ? (uint32_t)(mr * (C2 / 32) + nb / 16) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbi, srs, (int)so, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbg, srs, (int)(so == 0x80000000u ? so : so + 1u), 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // the row's other 16 columns of every fragment are in lane l ^ 32
@@ -1338,8 +1402,11 @@ hipError_t launch_dswiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo
   static std::atomic<bool> attr_set[64];
   const bool cached = dev.device >= 0 && dev.device < 64;
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiDswiglu, GS>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiDswiglu, GS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiDswigluQ, GS>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
   }
@@ -1353,8 +1420,12 @@ hipError_t launch_dswiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo
   q.ksplit = 1;
   q.partial = nullptr;
   q.tile_limit = 0;
-  hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiDswiglu, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s,
-                     q);
+  if (p.q_out != nullptr)
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiDswigluQ, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem,
+                       s, q);
+  else
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiDswiglu, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem,
+                       s, q);
   return hipGetLastError();
 }
 

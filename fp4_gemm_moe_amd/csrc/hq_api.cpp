@@ -195,7 +195,7 @@ hq_status hq_group_wise_quant(void* stream, int32_t mode, const uint16_t* x, int
 }
 
 // A caller workspace: null with 0 bytes (unsplit), else 16-byte aligned.
-hq_status check_workspace(const void* ws, uint64_t bytes, const char* what) {
+static hq_status check_workspace(const void* ws, uint64_t bytes, const char* what) {
   if (bytes > 0 && ws == nullptr) return fail(HQ_ERR_NULL, "%s: workspace is NULL but workspace_bytes > 0", what);
   if (ws != nullptr && !aligned16(ws)) return fail(HQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", what);
   return HQ_OK;
@@ -435,13 +435,13 @@ hq_status hq_group_contiguous_gemm_swiglu_quant(void* stream, int32_t mode, cons
   return launched(hq::launch_gemm_swiglu((hipStream_t)stream, p, dev), what);
 }
 
-hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uint8_t* a,
-                                           const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
-                                           const int32_t* group_end, int32_t num_groups,
-                                           const uint16_t* c, const float* alpha, const float* beta,
-                                           const float* prob, float* dprob, uint16_t* d,
-                                           int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
-  const char* what = "hq_group_contiguous_gemm_dswiglu";
+// Shared by the BF16 and the row-quantised dSwiGLU calls (exactly one of d
+// and dq is set).
+static hq_status dswiglu_call(const char* what, void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,
+                       const uint8_t* b, const uint8_t* sfb, const int32_t* group_end, int32_t num_groups,
+                       const uint16_t* c, const float* alpha, const float* beta, const float* prob, float* dprob,
+                       uint16_t* d, uint8_t* dq, uint8_t* dsf, int64_t m_total, int64_t n, int64_t k,
+                       int32_t cu_limit) {
   if (mode != HQ_MXFP8 && mode != HQ_MXFP4)
     return fail(HQ_ERR_MODE, "%s: MXFP8 or MXFP4 codes only (got %d)", what, mode);
   if (num_groups < 1 || num_groups > 1024)
@@ -449,13 +449,17 @@ hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uin
   if (n % 32 != 0) return fail(HQ_ERR_SHAPE, "%s: n=%lld must be a multiple of 32", what, (long long)n);
   if (n > 0 && n * 1024 >= ((int64_t)1 << 31))
     return fail(HQ_ERR_SHAPE, "%s: n=%lld too large (n * 1024 must be below 2^31)", what, (long long)n);
-  // alpha here is the per-group GEMM scale (entering squared), not the NVFP4 alpha
-  GemmCheck cc{mode, a, sfa, b, sfb, nullptr, nullptr, d, m_total, n, k, num_groups, what};
+  // alpha here is the per-group GEMM scale (entering squared), not the NVFP4
+  // alpha; the output check takes whichever output the call has
+  const void* out = dq != nullptr ? static_cast<const void*>(dq) : static_cast<const void*>(d);
+  GemmCheck cc{mode, a, sfa, b, sfb, nullptr, nullptr, static_cast<const uint16_t*>(out), m_total, n, k,
+               num_groups, what};
   bool noop;
   hq_status st = check_gemm(cc, &noop);
   if (st != HQ_OK) return st;
   if (noop) return ok();
   if (!group_end || !c || !prob || !dprob) return fail(HQ_ERR_NULL, "%s: group_end, c, prob and dprob are required", what);
+  if (dq != nullptr && dsf == nullptr) return fail(HQ_ERR_NULL, "%s: dsf is required", what);
   if (!aligned16(c)) return fail(HQ_ERR_ALIGN, "%s: c must be 16-byte aligned", what);
   if ((reinterpret_cast<uintptr_t>(prob) | reinterpret_cast<uintptr_t>(dprob)) & 3u)
     return fail(HQ_ERR_ALIGN, "%s: prob and dprob must be 4-byte aligned", what);
@@ -470,6 +474,8 @@ hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uin
   p.prob = prob;
   p.dprob = dprob;
   p.d_out = d;
+  p.q_out = dq;
+  p.sf_out = dsf;
   if (!hq::gemm_dswiglu_supported(p)) {
     if ((reinterpret_cast<uintptr_t>(sfa) | reinterpret_cast<uintptr_t>(sfb)) & 3)
       return fail(HQ_ERR_ALIGN, "%s: sfa and sfb must be 4-byte aligned", what);
@@ -479,6 +485,28 @@ hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uin
   hq::DeviceInfo dev;
   if ((st = current_device(&dev)) != HQ_OK) return st;
   return launched(hq::launch_gemm_dswiglu((hipStream_t)stream, p, dev), what);
+}
+
+hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode, const uint8_t* a,
+                                           const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                           const int32_t* group_end, int32_t num_groups,
+                                           const uint16_t* c, const float* alpha, const float* beta,
+                                           const float* prob, float* dprob, uint16_t* d,
+                                           int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
+  return dswiglu_call("hq_group_contiguous_gemm_dswiglu", stream, mode, a, sfa, b, sfb, group_end, num_groups, c,
+                      alpha, beta, prob, dprob, d, nullptr, nullptr, m_total, n, k, cu_limit);
+}
+
+hq_status hq_group_contiguous_gemm_dswiglu_quant(void* stream, int32_t mode, const uint8_t* a,
+                                                 const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                                 const int32_t* group_end, int32_t num_groups,
+                                                 const uint16_t* c, const float* alpha, const float* beta,
+                                                 const float* prob, float* dprob, uint8_t* dq, uint8_t* dsf,
+                                                 int64_t m_total, int64_t n, int64_t k, int32_t cu_limit) {
+  const char* what = "hq_group_contiguous_gemm_dswiglu_quant";
+  if (dq == nullptr && m_total > 0 && n > 0) return fail(HQ_ERR_NULL, "%s: dq is required", what);
+  return dswiglu_call(what, stream, mode, a, sfa, b, sfb, group_end, num_groups, c, alpha, beta, prob, dprob,
+                      nullptr, dq, dsf, m_total, n, k, cu_limit);
 }
 
 hq_status hq_group_masked_gemm(void* stream, int32_t mode, const uint8_t* a, const uint8_t* sfa,

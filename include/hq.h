@@ -328,6 +328,33 @@ hq_status hq_group_contiguous_gemm_dswiglu(void* stream, int32_t mode,
                                            int64_t k, int32_t cu_limit);
 
 /*
+ * hq_group_contiguous_gemm_dswiglu with a row-quantised D (the same page's
+ * optional output quantisation, Step 3, read with this library's MXFP8
+ * rule): instead of BF16 d, every row's 32-column blocks of D (one input or
+ * gate block each) are quantised from their BF16 values exactly as
+ * hq_group_wise_quant(HQ_MXFP8) quantises BF16 rows -- per block a UE8M0
+ * scale s = clamp(floor(log2 amax) - 8, -127, 127) and E4M3 codes of
+ * D / 2^s (nearest even, saturating).  So dq / dsf equal hq_group_wise_quant
+ * applied to the d of hq_group_contiguous_gemm_dswiglu.  (The page's own FP8
+ * recipe, a normalisation constant times the block amax times a reciprocal
+ * maximum with 128x4 scale atoms, is not implemented.)
+ *   dq [m_total, 2n] u8 E4M3 codes (16-byte aligned); dsf [m_total, 2n / 32]
+ *   u8 UE8M0 scales; every other argument as hq_group_contiguous_gemm_dswiglu.
+ * Rows at or past the last end are not written (dq, dsf nor dprob).  No
+ * workspace is used.
+ */
+hq_status hq_group_contiguous_gemm_dswiglu_quant(void* stream, int32_t mode,
+                                                 const uint8_t* a, const uint8_t* sfa,
+                                                 const uint8_t* b, const uint8_t* sfb,
+                                                 const int32_t* group_end,
+                                                 int32_t num_groups, const uint16_t* c,
+                                                 const float* alpha, const float* beta,
+                                                 const float* prob, float* dprob,
+                                                 uint8_t* dq, uint8_t* dsf,
+                                                 int64_t m_total, int64_t n, int64_t k,
+                                                 int32_t cu_limit);
+
+/*
  * Grouped-masked GEMM (HALOps "GEMM" page, group_masked_gemm section): expert
  * e owns the slot of rows [e * max_m, (e + 1) * max_m); only its first
  * min(masked_m[e], max_m) rows are computed and written (padded rows are

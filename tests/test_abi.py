@@ -213,3 +213,17 @@ def test_dswiglu_rejects_before_launch(lib):
     assert f(*args(dprob=NUL)) == -1
     assert f(*args(c=MIS)) == -3
     assert f(*args(d=MIS)) == -3
+
+
+def test_dswiglu_quant_rejects_before_launch(lib):
+    f = lib.hq_group_contiguous_gemm_dswiglu_quant
+    args = lambda mode=0, n=64, k=512, c=A, dprob=A, dq=A, dsf=A: (
+        None, mode, A, A, A, A, A, 4, c, NUL, NUL, A, dprob, dq, dsf, 64, n, k, 0)
+    assert f(*args(mode=2)) == -4              # NVFP4: not this call
+    assert f(*args(n=48)) == -2                # n % 32
+    assert f(*args(k=128)) == -2               # one MXFP8 K step
+    assert f(*args(dq=NUL)) == -1
+    assert f(*args(dsf=NUL)) == -1
+    assert f(*args(c=NUL)) == -1
+    assert f(*args(dq=MIS)) == -3
+    assert f(*args(c=MIS)) == -3

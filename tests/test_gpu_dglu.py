@@ -17,6 +17,10 @@ grouped GEMM with the dSwiGLU epilogue; cuDNN FE "Grouped GEMM + dGLU
   accumulates onto what it held.
 * The full backward MoE shape (32 experts, 65536 routed rows, K = 4096,
   N = 1536): sampled rows of four experts against the oracle.
+* The row-quantised form (hq_group_contiguous_gemm_dswiglu_quant): its codes
+  and scales equal the MXFP8 quantisation of the BF16 call's D, bit for bit,
+  on every written row (the oracle's too where D is integer-exact); rows past
+  the last end keep their sentinels; dprob within the same bound.
 """
 import numpy as np
 import pytest
@@ -58,6 +62,29 @@ def _run(mode, a, sfa, b, sfb, ends, c, prob, alpha, beta, dprob0, dev, cu_limit
     return U.host_bits(d), dprob.cpu().numpy()
 
 
+def _run_q(mode, a, sfa, b, sfb, ends, c, prob, alpha, beta, dprob0, dev):
+    M, N = c.shape[0], b.shape[1]
+    dq = torch.full((M, 2 * N), 0xA5, dtype=torch.uint8, device=dev)
+    dsf = torch.full((M, 2 * N // 32), 0x5A, dtype=torch.uint8, device=dev)
+    dprob = torch.from_numpy(np.asarray(dprob0, np.float32)).to(dev)
+    hq.hq_group_contiguous_gemm_dswiglu_quant(
+        mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b, dev), U.dev_u8(sfb, dev), U.dev_i32(ends, dev),
+        U.dev_bf16(c, dev), torch.from_numpy(np.asarray(prob, np.float32)).to(dev), dprob, dq, dsf,
+        alpha=None if alpha is None else torch.from_numpy(np.asarray(alpha, np.float32)).to(dev),
+        beta=None if beta is None else torch.from_numpy(np.asarray(beta, np.float32)).to(dev))
+    torch.cuda.synchronize()
+    return U.host_u8(dq), U.host_u8(dsf), dprob.cpu().numpy()
+
+
+def _check_quantised(d_bits, q, sf, written, what):
+    """Codes / scales of the written rows = MXFP8 quantisation of the BF16 D
+    (bit for bit); the other rows keep the sentinels."""
+    wq, ws = Q.mx_quant_bf16(d_bits[written], "mxfp8")
+    assert np.array_equal(q[written], wq), f"{what}: {np.sum(q[written] != wq)} codes differ"
+    assert np.array_equal(sf[written], ws), f"{what}: {np.sum(sf[written] != ws)} scales differ"
+    assert np.all(q[~written] == 0xA5) and np.all(sf[~written] == 0x5A), f"{what}: rows past the end written"
+
+
 INT_CASES = [("mxfp8", (40, 0, 300, 17), 96, 512), ("mxfp8", (256, 33), 320, 384),
              ("mxfp4", (40, 0, 300, 17), 96, 512), ("mxfp4", (129, 1), 64, 768)]
 
@@ -97,6 +124,13 @@ def test_dswiglu_integer_exact(case):
     assert np.array_equal(got, want), f"{np.sum(got != want)} of {got.size} D values differ"
     assert np.array_equal(gp[written].astype(np.float64), wp[written]), "dprob differs"
     assert np.all(gp[~written] == 0.0)
+    # the row-quantised form: the oracle's codes and scales, exactly
+    q, sf, gp2 = _run_q(mode, a, sfa, b, sfb, ends, cb, prob, alpha, beta, dprob0, dev)
+    oq, osf, _, _ = DG.grouped_gemm_dswiglu_quant(mode, a, sfa, b, sfb, ends, cb, prob, alpha, beta)
+    assert np.array_equal(q[written], oq[written]) and np.array_equal(sf[written], osf[written]), \
+        "row-quantised D differs from the oracle"
+    _check_quantised(got, q, sf, written, "int-exact")
+    assert np.array_equal(gp2[written].astype(np.float64), wp[written]), "dprob of the quantised form differs"
 
 
 def _random_case(mode, counts, N, K, seed, with_ab=True):
@@ -163,6 +197,10 @@ def test_dswiglu_random_against_oracle(case):
     assert np.array_equal(gp[~written], dprob0[~written]), "dprob past the last end changed"
     _check(mode, a, sfa, b, sfb, ends, c, prob, alpha, beta, dprob0, got[written], gp[written],
            f"{mode} N{N} K{K}")
+    q, sf, gp2 = _run_q(mode, a, sfa, b, sfb, ends, c, prob, alpha, beta, dprob0, dev)
+    _check_quantised(got, q, sf, written, f"{mode} N{N} K{K} quantised")
+    _check(mode, a, sfa, b, sfb, ends, c, prob, alpha, beta, dprob0, got[written], gp2[written],
+           f"{mode} N{N} K{K} (dprob of the quantised form)")
 
 
 def test_dswiglu_without_alpha_beta():
@@ -190,6 +228,13 @@ def test_dswiglu_rejects_what_it_cannot_run():
     assert lib.hq_group_contiguous_gemm_dswiglu(*args(0, 48, 512)) == -2      # n % 32
     assert lib.hq_group_contiguous_gemm_dswiglu(*args(0, 64, 128)) == -2      # one K step
     assert lib.hq_group_contiguous_gemm_dswiglu(*args(1, 64, 256)) == -2      # one FP4 K step
+    qargs = lambda mode, n, k, dq, dsf: (st, mode, P(z), P(z), P(z), P(z), P(z), 1, P(z), None, None, P(f), P(f),
+                                         dq, dsf, 8, n, k, 0)
+    fq = lib.hq_group_contiguous_gemm_dswiglu_quant
+    assert fq(*qargs(2, 64, 512, P(z), P(z))) == -4          # NVFP4
+    assert fq(*qargs(0, 64, 512, None, P(z))) == -1          # no dq
+    assert fq(*qargs(0, 64, 512, P(z), None)) == -1          # no dsf
+    assert fq(*qargs(0, 48, 512, P(z), P(z))) == -2          # n % 32
 
 
 def test_dswiglu_moe_backward_full_size_sampled():
@@ -228,5 +273,21 @@ def test_dswiglu_moe_backward_full_size_sampled():
         _check("mxfp8", ac, asc, wc[None], wsc[None], one, d["c"][rows], d["prob"][rows], d["alpha"][g:g + 1],
                d["beta"][g:g + 1], np.zeros(len(rows), np.float32), U.host_bits(out[rt]), dprob[rt].cpu().numpy(),
                f"expert {g} (count {c_})")
-    del qa, qw, c, out
+    # the row-quantised form at full size: codes / scales of every sampled row
+    # = MXFP8 quantisation of the BF16 call's D
+    dq = torch.full((R, 2 * N), 0xA5, dtype=torch.uint8, device=dev)
+    dsf = torch.full((R, 2 * N // 32), 0x5A, dtype=torch.uint8, device=dev)
+    hq.hq_group_contiguous_gemm_dswiglu_quant("mxfp8", qa, sa, qw.view(E, N, K), sw.view(E, N, K // 32),
+                                              U.dev_i32(ends, dev), c, prob, torch.zeros_like(dprob), dq, dsf,
+                                              alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.integers(0, R, 64), [0, R - 1], starts[np.asarray(counts) > 0]]))
+    rt = torch.from_numpy(rows.astype(np.int64)).to(dev)
+    valid = np.zeros(R, bool)
+    for g in range(E):
+        valid[int(starts[g]):int(ends[g])] = True      # padded rows are rows of their group too
+    sel = valid[rows]
+    _check_quantised(U.host_bits(out[rt])[sel], U.host_u8(dq[rt])[sel], U.host_u8(dsf[rt])[sel],
+                     np.ones(int(sel.sum()), bool), "full size, quantised")
+    del qa, qw, c, out, dq, dsf
     torch.cuda.empty_cache()
