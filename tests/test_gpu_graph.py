@@ -5,8 +5,12 @@ Every tensor -- inputs, outputs, the K-split workspace, the pointer arrays of
 the discrete-weights call -- is allocated before capture; the captured
 sequence is MXFP8 activation quantisation, NVFP4 quantisation with its amax
 pass, the grouped gate|up GEMM with the SwiGLU + re-quant epilogue, a K-split
-dense GEMM (workspace), a tail-split dense GEMM (workspace, CU limit) and the
-discrete-weights grouped GEMM.  The graph is replayed several times with the
+dense GEMM (workspace), a tail-split dense GEMM (workspace, CU limit), the
+discrete-weights grouped GEMM, a K-split batch GEMM (workspace), the masked
+grouped GEMM, the standalone SwiGLU + re-quant and the backward dSwiGLU GEMM
+in both output forms (dprob cleared by a fill kernel inside the graph; its
+FP32 atomic adds have no fixed order, so dprob is compared within 1e-5
+relative, everything else bit for bit).  The graph is replayed several times with the
 program's own eager work (outputs overwritten, other launches) and
 synchronisations between replays; every replay must give the eager results
 bit for bit.  The library records no memset node (its counters and the
@@ -61,10 +65,37 @@ def _setup(dev):
     st["sfbs"] = [st["wsf"][g].clone() for g in range(E)]
     st["bp"], st["sp"] = hq.ptr_arrays("mxfp8", st["bs"], st["sfbs"], 2 * H, K)
     st["pout"] = torch.empty(R, 2 * H, dtype=torch.bfloat16, device=dev)
+    # batch: 3 x 64 x 256 x 4096 (K split into the workspace)
+    Bn, bm, bn, bk = 3, 64, 256, 4096
+    qa, sa, _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (Bn * bm, bk)), dev), "mxfp8")
+    qb, sb, _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (Bn * bn, bk), 0.05), dev), "mxfp8")
+    st["ba"], st["bsa"] = qa.view(Bn, bm, bk), sa.view(Bn, bm, bk // 32)
+    st["bb"], st["bsb"] = qb.view(Bn, bn, bk), sb.view(Bn, bn, bk // 32)
+    st["bout"] = torch.empty(Bn, bm, bn, dtype=torch.bfloat16, device=dev)
+    st["bws"] = hq.gemm_workspace("mxfp8", bm, bn, bk, batch=Bn, device=dev)
+    # masked: 4 slots of 64 rows (counts 10, 0, 64, 33), K = 512, N = 2H
+    mq, msf, _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (E * 64, K)), dev), "mxfp8")
+    st["ma"], st["msa"] = mq, msf
+    st["mcnt"] = U.dev_i32(np.array([10, 0, 64, 33], np.int64), dev)
+    st["mout"] = torch.empty(E * 64, 2 * H, dtype=torch.bfloat16, device=dev)
+    # standalone SwiGLU + re-quant of a [R, 2H] BF16 gate|up buffer
+    st["gu"] = U.dev_bf16(synth.normal_bf16(rng, (R, 2 * H)), dev)
+    st["sq"] = torch.empty(R, H, dtype=torch.uint8, device=dev)
+    st["ssf"] = torch.empty(R, H // 32, dtype=torch.uint8, device=dev)
+    # backward dSwiGLU: R = aq * wq[g]^T (n = 2H), C [R, 4H], prob [R]
+    st["cc"] = U.dev_bf16(synth.normal_bf16(rng, (R, 4 * H)), dev)
+    st["prob"] = torch.from_numpy(rng.random(R).astype(np.float32)).to(dev)
+    st["dprob"] = torch.empty(R, dtype=torch.float32, device=dev)
+    st["dprobq"] = torch.empty(R, dtype=torch.float32, device=dev)
+    st["dd"] = torch.empty(R, 4 * H, dtype=torch.bfloat16, device=dev)
+    st["dq"] = torch.empty(R, 4 * H, dtype=torch.uint8, device=dev)
+    st["dsf"] = torch.empty(R, 4 * H // 32, dtype=torch.uint8, device=dev)
     return st
 
 
-OUTS = ["aq", "asf", "nq", "nsf", "ng", "yq", "ysf", "dout", "tout", "pout"]
+OUTS = ["aq", "asf", "nq", "nsf", "ng", "yq", "ysf", "dout", "tout", "pout", "bout", "mout", "sq", "ssf",
+        "dd", "dq", "dsf"]
+CLOSE = ["dprob", "dprobq"]
 
 
 def _calls(st):
@@ -77,6 +108,15 @@ def _calls(st):
                      workspace=st["tws"])
     hq.hq_group_contiguous_gemm_ptr_array("mxfp8", st["aq"], st["asf"], st["bp"], st["sp"], st["ge"],
                                           st["pout"], n=st["pout"].shape[1])
+    hq.hq_batch_gemm("mxfp8", st["ba"], st["bsa"], st["bb"], st["bsb"], st["bout"], workspace=st["bws"])
+    hq.hq_group_masked_gemm("mxfp8", st["ma"], st["msa"], st["wq"], st["wsf"], st["mcnt"], st["mout"], 64)
+    hq.hq_fused_swiglu_quant("mxfp8", st["gu"], st["sq"], st["ssf"], 4, group_end=st["ge"], valid=st["valid"])
+    st["dprob"].zero_()
+    st["dprobq"].zero_()
+    hq.hq_group_contiguous_gemm_dswiglu("mxfp8", st["aq"], st["asf"], st["wq"], st["wsf"], st["ge"], st["cc"],
+                                        st["prob"], st["dprob"], st["dd"])
+    hq.hq_group_contiguous_gemm_dswiglu_quant("mxfp8", st["aq"], st["asf"], st["wq"], st["wsf"], st["ge"],
+                                              st["cc"], st["prob"], st["dprobq"], st["dq"], st["dsf"])
 
 
 def _bits(t):
@@ -84,11 +124,11 @@ def _bits(t):
 
 
 def _snapshot(st):
-    return {k: st[k].clone() for k in OUTS}
+    return {k: st[k].clone() for k in OUTS + CLOSE}
 
 
 def _scribble(st):
-    for k in OUTS:
+    for k in OUTS + CLOSE:
         v = st[k]
         if v.dtype == torch.float32:
             v.fill_(-3.0)
@@ -98,7 +138,8 @@ def _scribble(st):
 
 def test_graph_capture_and_replay_equal_eager():
     dev = U.require_gpu()
-    U.banner("graph capture: quant, nvfp4 quant, gemm+swiglu, k-split, tail split, ptr-array")
+    U.banner("graph capture: quant, nvfp4 quant, gemm+swiglu, k-split, tail split, ptr-array, batch, masked, "
+             "swiglu, dswiglu (bf16 and row-quantised)")
     st = _setup(dev)
     _scribble(st)                   # rows a call does not write hold the fill byte in every run
     _calls(st)                      # eager run (also sets the kernels' launch attributes)
@@ -118,10 +159,14 @@ def test_graph_capture_and_replay_equal_eager():
         torch.cuda.synchronize()
         for k in OUTS:
             assert torch.equal(_bits(st[k]), _bits(want[k])), f"replay {rep}: {k} differs from the eager run"
+        for k in CLOSE:
+            assert torch.allclose(st[k], want[k], rtol=1e-5, atol=1e-6), f"replay {rep}: {k}"
         # eager work between replays: the same calls outside the graph, then other launches
         _calls(st)
         torch.cuda.synchronize()
         for k in OUTS:
             assert torch.equal(_bits(st[k]), _bits(want[k])), f"eager run after replay {rep}: {k}"
+        for k in CLOSE:
+            assert torch.allclose(st[k], want[k], rtol=1e-5, atol=1e-6), f"eager run after replay {rep}: {k}"
         torch.randn(1 << 20, device=dev).sum().item()
     del g
