@@ -316,14 +316,8 @@ def run_permute(args, torch, hq, synth):
     imap = torch.empty(T, topk, dtype=torch.int32, device=dev)
     nums = torch.empty(E, dtype=torch.int32, device=dev)
     f = lambda: hq.hq_prefill_permute_to_masked_gemm(x, scale, ids, E, M, px, osf, imap, nums)
-    timer = Timer(torch)
-    for _ in range(args.warmup):
-        f()
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        timer.mark("permute", f)
-    torch.cuda.synchronize()
-    ms = timer.mean_ms("permute")
+    _, us = _launch_us(torch, [f], reps=max(args.steps, 5), warm=args.warmup)
+    ms = us * 1e-3
     placed = int(nums.sum().item())
     # read x, scales, ids; write the placed rows and scale rows, the map, the counts
     bytes_ = T * (2 * H + H // 128 + 8 * topk) + placed * (2 * H + H // 32) + 4 * T * topk + 4 * E
