@@ -167,10 +167,13 @@ struct Lay {
 // SYNC, where the A fragment of row 1 is first read (behind a second
 // workgroup barrier), so they land up to half a step later.  Measured on the
 // grouped, fused and backward MXFP8 GEMMs: 4-5 % faster than all loads in the
-// first half of the step, all waited for at its end.
-template <int FMT, bool GS>
+// first half of the step, all waited for at its end.  ON = false keeps an
+// instantiation on the v-major order with every load in the first half of the
+// step (the row-quantising dSwiGLU epilogue, which already holds 256 VGPRs:
+// the i-major loop's B fragments of both sub-steps spill there, 12 % slower).
+template <int FMT, bool GS, bool ON = true>
 struct Sched {
-  static constexpr bool LATE = FMT == 0 && GS;
+  static constexpr bool LATE = FMT == 0 && GS && ON;
   static constexpr int SLOTS = 32;              // MFMAs of a step
   static constexpr int SYNC = 4;                // slot of the mid-step wait and barrier
   static constexpr int N_LATE = 6;              // late loads per wave, the last ones issued
@@ -405,8 +408,9 @@ __device__ __forceinline__ LoadOffsets<FMT, PAIRED> make_offsets(const GemmArgs&
 // operand loads in the same order.  part -2 issues only grouped scale loads:
 // the step calls it ahead of its matrix instructions, because the branch on
 // the step's place in its scale group would otherwise let the compiler sink
-// the instructions before it below it and bunch up the operand loads.
-template <int FMT, bool GS, bool PAIRED>
+// the instructions before it below it and bunch up the operand loads.  SCH:
+// the ON flag of the instantiation's load schedule (Sched).
+template <int FMT, bool GS, bool PAIRED, bool SCH = true>
 __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT, PAIRED>& o, int k, uint32_t base,
                                       uint32_t lds0, int w, int part = -1, int slots = 1) {
   using C = Cfg<FMT>;
@@ -420,10 +424,10 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT, PAI
   if (part != -2) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      if (part < 0 || part == Sched<FMT, GS>::slot(i, slots, 2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
+      if (part < 0 || part == Sched<FMT, GS, SCH>::slot(i, slots, 2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      if (part < 0 || part == Sched<FMT, GS>::slot(LOADS + i, slots, 2 * LOADS))
+      if (part < 0 || part == Sched<FMT, GS, SCH>::slot(LOADS + i, slots, 2 * LOADS))
         dma16(rb, PAIRED ? o.btile[i] : o.tile[i], lb + i * WAVES * 1024);
   }
   // Scales.  With four waves wave w loads rows [64 w, 64 w + 64) of A and of
@@ -628,7 +632,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // runs the epilogue, whose stores then fall outside the tile's bounds.
   bool active = true;
   constexpr int kLoadRows = 4;
-  using Sc = Sched<FMT, GS>;
+  constexpr bool kSch = EPI != kEpiDswigluQ;
+  using Sc = Sched<FMT, GS, kSch>;
   // A tile's step 0 (kFirst) starts its accumulators from zero: its first
   // sub-step's matrix instructions take a zero accumulator operand, so the
   // accumulators are never cleared separately.  (A wave that skips its matrix
@@ -822,8 +827,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
-  issue<FMT, GS, PAIRED>(tl, lo, 0, smem_lds, smem_lds, w);
-  issue<FMT, GS, PAIRED>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
+  issue<FMT, GS, PAIRED, kSch>(tl, lo, 0, smem_lds, smem_lds, w);
+  issue<FMT, GS, PAIRED, kSch>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
   wait_vm<L::OPS1>();
   bar();
   // the scale words of step k of tile `tl` in stage `stage`
@@ -862,7 +867,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     for (int k = 1; k + 1 < tl.nk; ++k) {
       const uint32_t nxt = smem_lds + (st ^ 1) * L::STAGE;
       step(smem + st * L::STAGE, scl(tl, k, st),
-           [&](int part, int slots) { issue<FMT, GS, PAIRED>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
+           [&](int part, int slots) { issue<FMT, GS, PAIRED, kSch>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
            [&]() {
              // this step's late loads, issued in step k - 1 (step 1's loads
              // were issued whole ahead of the tile and have landed): since
@@ -887,7 +892,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG, TCOLS);
       // the scale buffer after this tile's last scale group
       tn.sg = (tl.sg + tl.nk / L::SPG) & 1;
-      issue<FMT, GS, PAIRED>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
+      issue<FMT, GS, PAIRED, kSch>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
     }
     step(smem + st * L::STAGE, scl(tl, tl.nk - 1, st), [](int, int) {},
          [&]() {
@@ -902,7 +907,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
          std::false_type{});
     pin();
     bar();                            // stage `st` is free
-    if (has_next) issue<FMT, GS, PAIRED>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
+    if (has_next) issue<FMT, GS, PAIRED, kSch>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
 
     if constexpr (EPI == kEpiSplit) {
       // ---- K-split epilogue: this slice's FP32 partial tile to
