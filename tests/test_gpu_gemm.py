@@ -409,6 +409,37 @@ def test_group_contiguous(mode, case):
 
 
 @pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
+def test_group_contiguous_many_tiles_per_workgroup(mode):
+    """A CU limit of 3 makes each workgroup walk about five tiles in turn, each
+    of four K steps (K = 512, whole 16-byte scale groups), so every tile
+    boundary carries the next tile's loads; partial last tiles leave waves
+    without rows.  Integer-valued operands: exact against the exact sums."""
+    dev = U.require_gpu()
+    counts, K, N, trailing = [128, 300, 0, 77, 256, 1, 200], 512, 512, 5
+    U.banner(f"contiguous {mode} many tiles per workgroup")
+    rng = np.random.default_rng(2024)
+    E = len(counts)
+    ends = np.cumsum(counts).astype(np.int32)
+    R = int(ends[-1]) + trailing
+    av, a, sfa = _int_operand(rng, R, K, mode, [-1, 0, 1])
+    bv, b, sfb = _int_operand(rng, E * N, K, mode, [-1, 0, 1])
+    alpha = torch.ones(E, dtype=torch.float32, device=dev) if mode == "nvfp4" else None
+    out = torch.full((R, N), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    hq.hq_group_contiguous_gemm(mode, U.dev_u8(a, dev), U.dev_u8(sfa, dev), U.dev_u8(b.reshape(E, N, -1), dev),
+                                U.dev_u8(sfb.reshape(E, N, -1), dev), U.dev_i32(ends, dev), out, alpha=alpha,
+                                cu_limit=3)
+    torch.cuda.synchronize()
+    got = U.host_bits(out)
+    assert np.all(got[int(ends[-1]):] == SENTINEL), "rows after the last group were written"
+    lo = 0
+    for g in range(E):
+        hi = int(ends[g])
+        want = F.bf16_round((av[lo:hi] @ bv[g * N:(g + 1) * N].T).astype(np.float64))
+        assert np.array_equal(got[lo:hi], want), f"group {g}: {np.sum(got[lo:hi] != want)} differ"
+        lo = hi
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
 def test_group_masked_matches_contiguous_with_garbage_padding(mode):
     dev = U.require_gpu()
     E, Mmax, K, N = 6, 48, 256, 64
