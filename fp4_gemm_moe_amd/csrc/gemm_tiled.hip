@@ -85,6 +85,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
                "s"(lds) : "memory");
 }
+// The same with the non-temporal cache policy, for operands read exactly
+// once: a microbenchmark streaming a weight tensor in a tile's row pattern
+// (256 rows x 128 bytes per step, one workgroup per CU) reads 7.0 TB/s with
+// it and 4.6 TB/s without.
+__device__ __forceinline__ void dma16nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r),
+               "s"(lds) : "memory");
+}
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
                "s"(lds) : "memory");
@@ -409,8 +417,9 @@ __device__ __forceinline__ LoadOffsets<FMT, PAIRED> make_offsets(const GemmArgs&
 // the step calls it ahead of its matrix instructions, because the branch on
 // the step's place in its scale group would otherwise let the compiler sink
 // the instructions before it below it and bunch up the operand loads.  SCH:
-// the ON flag of the instantiation's load schedule (Sched).
-template <int FMT, bool GS, bool PAIRED, bool SCH = true>
+// the ON flag of the instantiation's load schedule (Sched).  NTB: B's rows are
+// read with the non-temporal policy (each weight byte is read once).
+template <int FMT, bool GS, bool PAIRED, bool SCH = true, bool NTB = false>
 __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT, PAIRED>& o, int k, uint32_t base,
                                       uint32_t lds0, int w, int part = -1, int slots = 1) {
   using C = Cfg<FMT>;
@@ -427,8 +436,10 @@ __device__ __forceinline__ void issue(const Tile& tl, const LoadOffsets<FMT, PAI
       if (part < 0 || part == Sched<FMT, GS, SCH>::slot(i, slots, 2 * LOADS)) dma16(ra, o.tile[i], la + i * WAVES * 1024);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      if (part < 0 || part == Sched<FMT, GS, SCH>::slot(LOADS + i, slots, 2 * LOADS))
-        dma16(rb, PAIRED ? o.btile[i] : o.tile[i], lb + i * WAVES * 1024);
+      if (part < 0 || part == Sched<FMT, GS, SCH>::slot(LOADS + i, slots, 2 * LOADS)) {
+        if constexpr (NTB) dma16nt(rb, PAIRED ? o.btile[i] : o.tile[i], lb + i * WAVES * 1024);
+        else dma16(rb, PAIRED ? o.btile[i] : o.tile[i], lb + i * WAVES * 1024);
+      }
   }
   // Scales.  With four waves wave w loads rows [64 w, 64 w + 64) of A and of
   // B; with eight, waves 0-3 those rows of A and waves 4-7 of B.
@@ -513,7 +524,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // forward activations C and writes D and the dprob row sums.
 constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4, kEpiDswigluQ = 5;
 
-template <int FMT, int EPI, bool GS>
+template <int FMT, int EPI, bool GS, bool NTB = false>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
   using L = Lay<FMT, GS>;
@@ -827,8 +838,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
-  issue<FMT, GS, PAIRED, kSch>(tl, lo, 0, smem_lds, smem_lds, w);
-  issue<FMT, GS, PAIRED, kSch>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
+  issue<FMT, GS, PAIRED, kSch, NTB>(tl, lo, 0, smem_lds, smem_lds, w);
+  issue<FMT, GS, PAIRED, kSch, NTB>(tl, lo, 1, smem_lds + L::STAGE, smem_lds, w);
   wait_vm<L::OPS1>();
   bar();
   // the scale words of step k of tile `tl` in stage `stage`
@@ -867,7 +878,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     for (int k = 1; k + 1 < tl.nk; ++k) {
       const uint32_t nxt = smem_lds + (st ^ 1) * L::STAGE;
       step(smem + st * L::STAGE, scl(tl, k, st),
-           [&](int part, int slots) { issue<FMT, GS, PAIRED, kSch>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
+           [&](int part, int slots) { issue<FMT, GS, PAIRED, kSch, NTB>(tl, lo, k + 1, nxt, smem_lds, w, part, slots); },
            [&]() {
              // this step's late loads, issued in step k - 1 (step 1's loads
              // were issued whole ahead of the tile and have landed): since
@@ -892,7 +903,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG, TCOLS);
       // the scale buffer after this tile's last scale group
       tn.sg = (tl.sg + tl.nk / L::SPG) & 1;
-      issue<FMT, GS, PAIRED, kSch>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
+      issue<FMT, GS, PAIRED, kSch, NTB>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
     }
     step(smem + st * L::STAGE, scl(tl, tl.nk - 1, st), [](int, int) {},
          [&]() {
@@ -907,7 +918,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
          std::false_type{});
     pin();
     bar();                            // stage `st` is free
-    if (has_next) issue<FMT, GS, PAIRED, kSch>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
+    if (has_next) issue<FMT, GS, PAIRED, kSch, NTB>(tn, lo, 1, smem_lds + st * L::STAGE, smem_lds, w);
 
     if constexpr (EPI == kEpiSplit) {
       // ---- K-split epilogue: this slice's FP32 partial tile to
@@ -1392,17 +1403,34 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   static std::atomic<bool> attr_set[64];
   const bool cached = dev.device >= 0 && dev.device < 64;
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiBf16, GS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiF16, GS>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<FMT, kEpiSplit, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              smem);
-    if (e != hipSuccess) return e;
+    const void* fns[] = {(const void*)mx_gemm_tiled<FMT, kEpiBf16, GS>, (const void*)mx_gemm_tiled<FMT, kEpiF16, GS>,
+                         (const void*)mx_gemm_tiled<FMT, kEpiSplit, GS>,
+                         (const void*)mx_gemm_tiled<FMT, kEpiBf16, GS, true>,
+                         (const void*)mx_gemm_tiled<FMT, kEpiF16, GS, true>,
+                         (const void*)mx_gemm_tiled<FMT, kEpiSplit, GS, true>};
+    for (const void* fn : fns) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      if (e != hipSuccess) return e;
+    }
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
   }
+  // Masked slots of at most BM rows: every weight tile is read by one m-tile
+  // only, by every CU at once, so the weights stream from HBM and their loads
+  // take the non-temporal policy (masked MXFP4 at E=64, K=7168, N=4096: 8-9 %
+  // faster).  Measured against it elsewhere: dense MXFP4 4096x17408x5120,
+  // whose weight tiles 16 m-tiles read, 12 % slower; dense 256x17408x5120
+  // (one m-tile, but K-split over a part of the CUs) 21 % slower.
+  const bool ntb = p.form == kMasked && p.slot_rows <= BM;
+  auto go = [&](auto epi, int64_t grid, const GemmArgs& q) {
+    constexpr int E = decltype(epi)::value;
+    if (ntb)
+      hipLaunchKernelGGL((mx_gemm_tiled<FMT, E, GS, true>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+    else
+      hipLaunchKernelGGL((mx_gemm_tiled<FMT, E, GS, false>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+  };
+  using EpiBf16 = std::integral_constant<int, kEpiBf16>;
+  using EpiF16 = std::integral_constant<int, kEpiF16>;
+  using EpiSplit = std::integral_constant<int, kEpiSplit>;
   const int64_t NT = (p.n + BN - 1) / BN;
   int64_t gm_upper;
   if (p.form == kContiguous) gm_upper = (p.m_rows + BM - 1) / BM + p.num_groups;
@@ -1438,18 +1466,14 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
     q1.ksplit = 1;
     q1.partial = nullptr;
     q1.tile_limit = (int32_t)(tiles - sp.rect_tiles);
-    if (q1.out_f16)
-      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
-                         smem, s, q1);
-    else
-      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid_full), dim3(Cfg<FMT>::THREADS),
-                         smem, s, q1);
+    if (q1.out_f16) go(EpiF16{}, grid_full, q1);
+    else go(EpiBf16{}, grid_full, q1);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
       int64_t g2 = sp.rect_tiles * sp.S;
       if (g2 > grid_full) g2 = grid_full;
       if (g2 >= 8) g2 -= g2 % 8;
-      hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)g2), dim3(Cfg<FMT>::THREADS), smem, s, q2);
+      go(EpiSplit{}, g2, q2);
       e = hipGetLastError();
     }
     if (e == hipSuccess) {
@@ -1473,12 +1497,9 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   if (tiles * q.ksplit < grid) grid = tiles * q.ksplit;
   if (grid >= 8) grid -= grid % 8;     // whole rounds over the 8 XCDs
   if (grid < 1) grid = 1;
-  if (q.ksplit > 1)
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiSplit, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
-  else if (q.out_f16)
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiF16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
-  else
-    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiBf16, GS>), dim3((unsigned)grid), dim3(Cfg<FMT>::THREADS), smem, s, q);
+  if (q.ksplit > 1) go(EpiSplit{}, grid, q);
+  else if (q.out_f16) go(EpiF16{}, grid, q);
+  else go(EpiBf16{}, grid, q);
   hipError_t e = hipGetLastError();
   if (q.ksplit > 1 && e == hipSuccess) {
     int64_t rgrid = (int64_t)cus * 4;
