@@ -439,13 +439,21 @@ def test_group_contiguous_many_tiles_per_workgroup(mode):
         lo = hi
 
 
+# Slots of at most 256 rows (one m-tile each: the weights are read once and
+# take the non-temporal load policy) and slots of 300 rows (two m-tiles each:
+# the default policy).
+MASKED_CASES = [(48, 256, 64, [48, 0, 13, 1, 30, 47]), (300, 512, 256, [300, 0, 257, 1, 130, 299])]
+
+
 @pytest.mark.parametrize("mode", ["mxfp8", "mxfp4", "nvfp4"])
-def test_group_masked_matches_contiguous_with_garbage_padding(mode):
+@pytest.mark.parametrize("case", MASKED_CASES, ids=lambda c: f"slot{c[0]}")
+def test_group_masked_matches_contiguous_with_garbage_padding(mode, case):
     dev = U.require_gpu()
-    E, Mmax, K, N = 6, 48, 256, 64
-    counts = np.array([48, 0, 13, 1, 30, 47], np.int32)
+    Mmax, K, N, cl = case
+    counts = np.array(cl, np.int32)
+    E = len(counts)
     rng = np.random.default_rng(9)
-    U.banner(f"masked {mode}")
+    U.banner(f"masked {mode} slots of {Mmax} rows")
     xa = synth.normal_bf16(rng, (int(counts.sum()), K))
     a_c, sfa_c, ga = _quant(xa, mode)
     xb = synth.normal_bf16(rng, (E * N, K), 0.05)
