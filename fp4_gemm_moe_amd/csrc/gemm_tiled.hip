@@ -562,15 +562,27 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   // gridDim tiles XCD x owns a contiguous run of tiles.  Rounds alternate
   // direction: in odd rounds the workgroup at slot s takes the round's tile
   // stride - 1 - s (a workgroup's tile index still grows round by round).
+  // Dense launches (one group, unsplit, the whole tile list) instead give XCD
+  // x the contiguous eighth [lo_x, tile_end) of the tile list, walked 32 tiles
+  // a round: its L2 then holds an eighth of the n-tiles' weights for the whole
+  // launch (dense MXFP4 4096x17408x5120: 3.5 % faster, MXFP8 2 %; the grouped
+  // and masked GEMMs ran 1-10 % slower with it, their groups' tiles being
+  // spread over the XCDs already).
   const int nxcd = gridDim.x >= 8 ? 8 : 1;
   const int per_xcd = gridDim.x / nxcd;
   const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
   const int stride = per_xcd * nxcd;
   if ((int)blockIdx.x >= stride) return;
-  auto tile_of = [&](int round) { return round * stride + ((round & 1) ? stride - 1 - slot : slot); };
+  const bool xmajor = p.form == kUniform && p.num_groups == 1 && p.ksplit <= 1 && p.tile_limit <= 0;
+  const int xi = (int)(blockIdx.x % nxcd), ci = (int)(blockIdx.x / nxcd);
+  const int lo_x = (int)((int64_t)total * xi / nxcd);
+  const int tile_end = xmajor ? (int)((int64_t)total * (xi + 1) / nxcd) : total;
+  auto tile_of = [&](int round) {
+    return xmajor ? lo_x + round * per_xcd + ci : round * stride + ((round & 1) ? stride - 1 - slot : slot);
+  };
   int round = 0;
   int t = tile_of(0);
-  if (t >= total) return;
+  if (t >= tile_end) return;
 
   const LoadOffsets<FMT, PAIRED> lo = make_offsets<FMT, PAIRED>(p, w, lane);
 
@@ -897,7 +909,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
     // last step: the next tile's step 0 goes into the other stage
     const int t_next = tile_of(round + 1);
-    const bool has_next = t_next < total;
+    const bool has_next = t_next < tile_end;
     Tile tn = tl;
     if (has_next) {
       tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG, TCOLS);
