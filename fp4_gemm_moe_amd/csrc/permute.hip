@@ -102,12 +102,17 @@ __global__ __launch_bounds__(kThreads) void permute_scatter(PermuteArgs a) {
     const int32_t* rows = prow + tl * a.topk;
     const int32_t* exps = pex + tl * a.topk;
     const uint4* src = reinterpret_cast<const uint4*>(a.x + t * a.row_bytes);
+    // the row is read once and each copy written once: both with the
+    // non-temporal policy (16384 BF16 tokens of 2048, top-8: 8 % faster)
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u* vsrc = reinterpret_cast<const v4u*>(src);
     for (int64_t c = lane; c < chunks; c += 64) {
-      const uint4 v = src[c];
+      const v4u v = __builtin_nontemporal_load(vsrc + c);
       for (int j = 0; j < a.topk; ++j) {
         const int32_t r = rows[j];
         if (r >= 0)
-          reinterpret_cast<uint4*>(a.out_x + ((int64_t)exps[j] * a.max_tokens + r) * a.row_bytes)[c] = v;
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<v4u*>(a.out_x + ((int64_t)exps[j] * a.max_tokens + r) * a.row_bytes) + c);
       }
     }
     // broadcast: source byte g128 (little-endian in int32 words) -> output
