@@ -524,7 +524,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // forward activations C and writes D and the dprob row sums.
 constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4, kEpiDswigluQ = 5;
 
-template <int FMT, int EPI, bool GS, bool NTB = false>
+// NOBIAS (the SwiGLU epilogue without a bias): the epilogue packs the
+// accumulators as they are instead of adding a zero bias to each.  The
+// result is the same: an accumulator is never -0 (the first matrix
+// instruction of a tile adds its products to +0), so adding +0 changes no
+// bit; the adds cost 0.7-1.5 % of the fused gate|up GEMM (interleaved A/B).
+template <int FMT, int EPI, bool GS, bool NTB = false, bool NOBIAS = false>
 __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p) {
   using C = Cfg<FMT>;
   using L = Lay<FMT, GS>;
@@ -1137,7 +1142,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(uniform_ptr(p.sf_out + tl.row0 * (H / 32))), (short)0,
           (int)ufirst((uint32_t)(vrows * (H / 32))), 0x00020000);
-      const uint16_t* bias = p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
+      const uint16_t* bias = !NOBIAS && p.bias ? p.bias + (int64_t)tl.g * p.n : nullptr;
       // lane-derived offsets from an opaque copy of the lane id, so that the
       // compiler computes them here instead of keeping them live through the
       // K loop (which runs out of registers)
@@ -1170,9 +1175,14 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
           for (int b = 0; b < 4; ++b) {
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
-              const uint32_t g2 = pack_bf16x2(acc[i][j][4 * b + r] + gb[b][r], acc[i][j][4 * b + r + 1] + gb[b][r + 1]);
-              const uint32_t u2 = pack_bf16x2(acc[i][j + 2][4 * b + r] + ub[b][r],
-                                              acc[i][j + 2][4 * b + r + 1] + ub[b][r + 1]);
+              uint32_t g2, u2;
+              if constexpr (NOBIAS) {
+                g2 = pack_bf16x2(acc[i][j][4 * b + r], acc[i][j][4 * b + r + 1]);
+                u2 = pack_bf16x2(acc[i][j + 2][4 * b + r], acc[i][j + 2][4 * b + r + 1]);
+              } else {
+                g2 = pack_bf16x2(acc[i][j][4 * b + r] + gb[b][r], acc[i][j][4 * b + r + 1] + gb[b][r + 1]);
+                u2 = pack_bf16x2(acc[i][j + 2][4 * b + r] + ub[b][r], acc[i][j + 2][4 * b + r + 1] + ub[b][r + 1]);
+              }
               y[b][r] = silu_mul(bf16_lo(g2), bf16_lo(u2));
               y[b][r + 1] = silu_mul(bf16_hi(g2), bf16_hi(u2));
             }
@@ -1530,8 +1540,11 @@ hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo&
   static std::atomic<bool> attr_set[64];
   const bool cached = dev.device >= 0 && dev.device < 64;
   if (!cached || !attr_set[dev.device].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<0, kEpiSwiglu, GS>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_tiled<0, kEpiSwiglu, GS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)mx_gemm_tiled<0, kEpiSwiglu, GS, false, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     if (cached) attr_set[dev.device].store(true, std::memory_order_release);
   }
@@ -1545,7 +1558,11 @@ hipError_t launch_swiglu_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo&
   q.ksplit = 1;
   q.partial = nullptr;
   q.tile_limit = 0;
-  hipLaunchKernelGGL((mx_gemm_tiled<0, kEpiSwiglu, GS>), dim3((unsigned)grid), dim3(Cfg<0>::THREADS), smem, s, q);
+  if (p.bias == nullptr)
+    hipLaunchKernelGGL((mx_gemm_tiled<0, kEpiSwiglu, GS, false, true>), dim3((unsigned)grid), dim3(Cfg<0>::THREADS),
+                       smem, s, q);
+  else
+    hipLaunchKernelGGL((mx_gemm_tiled<0, kEpiSwiglu, GS>), dim3((unsigned)grid), dim3(Cfg<0>::THREADS), smem, s, q);
   return hipGetLastError();
 }
 
