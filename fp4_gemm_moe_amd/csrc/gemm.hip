@@ -24,9 +24,11 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) 
   return launch_gemm_direct(s, p, dev);
 }
 
-uint64_t gemm_workspace_bytes(const GemmArgs& p, const DeviceInfo& dev) {
+uint64_t gemm_workspace_bytes(const GemmArgs& p, const DeviceInfo& dev, bool* stream_k) {
+  if (stream_k != nullptr) *stream_k = false;
   if (!use_tiled(p)) return 0;
   const SplitPlan sp = plan_split(p, dev);
+  if (stream_k != nullptr) *stream_k = sp.kind == kSplitStream;
   return sp.kind == kSplitNone ? 0 : sp.bytes;
 }
 

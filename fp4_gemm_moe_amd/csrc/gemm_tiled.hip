@@ -114,6 +114,7 @@ constexpr int BM = 256, BN = 256;
 constexpr int kMB = 8;                      // m-tiles per block of the tile order (make_tile)
 constexpr int SROW = 128;                   // bytes of a row per stage
 constexpr int kNV = 2;                      // format tag of the NVFP4 instantiation
+constexpr int kSkSpin = 1 << 20;            // polls of a stream-K flag before giving up (~1 s)
 
 template <int FMT>
 struct Cfg {
@@ -277,6 +278,7 @@ __device__ int build_tiled_table(const GemmArgs& p, TiledTable& t, int& n_heavy)
 struct Tile {
   int g;
   int nk, slice;                 // K steps of this tile (range), K-split slice
+  int sk0, sk1;                  // stream-K piece: K units [sk0, sk1) of the tile's units
   int sg;                        // scale buffer of the tile's first scale group (GS)
   int64_t row0, row_end, n0;
   int64_t vend;                  // end of the rows an epilogue writes (SwiGLU: the valid rows)
@@ -291,7 +293,7 @@ struct Tile {
 template <int FMT>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& tt, int total_gm,
                                           int n_heavy, int NT, int mt_per, int nk, int t, int unit,
-                                          int tile_cols) {
+                                          int tile_cols, int sk0 = 0, int sk1 = 0) {
   // K split: units are numbered slice-major, so that neighbouring units of
   // one slice share operand rows as without a split
   const int S = p.ksplit > 1 ? p.ksplit : 1;
@@ -335,8 +337,18 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& p, const TiledTable& t
   tl.sg = 0;
   tl.g = (int)ufirst((uint32_t)g);
   // this slice's K steps [k0, k1) of the nk steps, on multiples of `unit`
-  const int ng = nk / unit;
-  const int k0 = unit * (int)((int64_t)slice * ng / S), k1 = unit * (int)((int64_t)(slice + 1) * ng / S);
+  // (a stream-K piece: units [sk0, sk1) of `unit` steps)
+  int k0, k1;
+  if (sk1 > 0) {
+    k0 = unit * sk0;
+    k1 = unit * sk1;
+  } else {
+    const int ng = nk / unit;
+    k0 = unit * (int)((int64_t)slice * ng / S);
+    k1 = unit * (int)((int64_t)(slice + 1) * ng / S);
+  }
+  tl.sk0 = (int)ufirst((uint32_t)sk0);
+  tl.sk1 = (int)ufirst((uint32_t)sk1);
   tl.slice = (int)ufirst((uint32_t)slice);
   tl.nk = (int)ufirst((uint32_t)(k1 - k0));
   const int64_t kb = (int64_t)ufirst((uint32_t)k0) * SROW, ksb = (int64_t)ufirst((uint32_t)k0) * Cfg<FMT>::SB;
@@ -521,8 +533,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // PAIRED B rows) applies SwiGLU and the MXFP8 re-quant and writes codes and
 // scales of y instead of the gate|up output; kEpiDswiglu (the backward
 // GEMM, grouped-contiguous) applies the dSwiGLU derivative to R with the
-// forward activations C and writes D and the dprob row sums.
-constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4, kEpiDswigluQ = 5;
+// forward activations C and writes D and the dprob row sums; kEpiStream
+// (a dense stream-K launch) runs pieces of tiles: a piece that does not end
+// its tile hands its FP32 partial tile to the piece that does, which adds
+// it and writes the BF16 / binary16 output.
+constexpr int kEpiBf16 = 0, kEpiSplit = 1, kEpiSwiglu = 2, kEpiF16 = 3, kEpiDswiglu = 4, kEpiDswigluQ = 5,
+              kEpiStream = 6;
 
 // NOBIAS (the SwiGLU epilogue without a bias): the epilogue packs the
 // accumulators as they are instead of adding a zero bias to each.  The
@@ -578,13 +594,61 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   const int slot = (blockIdx.x % nxcd) * per_xcd + blockIdx.x / nxcd;
   const int stride = per_xcd * nxcd;
   if ((int)blockIdx.x >= stride) return;
-  const bool xmajor = p.form == kUniform && p.num_groups == 1 && p.ksplit <= 1 && p.tile_limit <= 0;
+  constexpr bool SKM = EPI == kEpiStream;
+  const bool xmajor = !SKM && p.form == kUniform && p.num_groups == 1 && p.ksplit <= 1 && p.tile_limit <= 0;
   const int xi = (int)(blockIdx.x % nxcd), ci = (int)(blockIdx.x / nxcd);
   const int lo_x = (int)((int64_t)total * xi / nxcd);
   const int tile_end = xmajor ? (int)((int64_t)total * (xi + 1) / nxcd) : total;
+  // Stream-K: the tiles' K steps, in tile order, are total * upt units of
+  // p.sk_unit steps; workgroup `slot` takes the units [u0, u1), at most one
+  // tile's worth (the launcher keeps total <= stride), so at most two pieces:
+  // the start of tile (u1 - 1) / upt first, then the end of tile u0 / upt.
+  // Consecutive slots share an XCD, so the pieces of a tile and of its
+  // neighbours in the tile order (which share B columns) meet in one L2.
+  // The pieces are recomputed where they are needed, from an opaque copy of
+  // the slot, so that none of it stays in registers through the K loop.
+  const int upt = SKM ? p.sk_upt : 1;
+  struct Piece {
+    int t, a, b;   // tile, K units [a, b) of its upt
+  };
+  auto sk_run = [&](int64_t& u0, int64_t& u1) {
+    int sl = slot;
+    asm volatile("" : "+s"(sl));
+    const int64_t tot = (int64_t)total * upt;
+    u0 = (int64_t)sl * tot / stride;
+    u1 = (int64_t)(sl + 1) * tot / stride;
+  };
+  auto piece = [&](int round) -> Piece {
+    Piece pc{total, 0, 0};
+    if constexpr (SKM) {
+      int64_t u0, u1;
+      sk_run(u0, u1);
+      if (u1 > u0 && u1 - u0 <= upt) {
+        const int tlo = (int)(u0 / upt), thi = (int)((u1 - 1) / upt);
+        if (round == 0) pc = thi > tlo ? Piece{thi, 0, (int)(u1 - (int64_t)thi * upt)}
+                                       : Piece{tlo, (int)(u0 - (int64_t)tlo * upt), (int)(u1 - (int64_t)tlo * upt)};
+        else if (round == 1 && thi > tlo) pc = Piece{tlo, (int)(u0 - (int64_t)tlo * upt), upt};
+      }
+    }
+    return pc;
+  };
+  // the second piece, kept in LDS through the first one's K loop
+  __shared__ int sk_second[3];
+  Piece sk_first{total, 0, 0};
+  if constexpr (SKM) {
+    sk_first = piece(0);
+    const Piece p1 = piece(1);
+    if (tid == 0) {
+      sk_second[0] = p1.t;
+      sk_second[1] = p1.a;
+      sk_second[2] = p1.b;
+    }
+  }
   auto tile_of = [&](int round) {
+    if constexpr (SKM) return round == 0 ? sk_first.t : total;
     return xmajor ? lo_x + round * per_xcd + ci : round * stride + ((round & 1) ? stride - 1 - slot : slot);
   };
+  const int kunit = SKM ? p.sk_unit : L::SPG;           // make_tile's K unit
   int round = 0;
   int t = tile_of(0);
   if (t >= tile_end) return;
@@ -851,7 +915,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     }
   };
 
-  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t, L::SPG, TCOLS);
+  Tile tl = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t, kunit, TCOLS, sk_first.a, sk_first.b);
   int st = 0;                                   // stage of the current step
   // first tile: steps 0 and 1 in flight, wait for step 0
   const uint32_t smem_lds = ufirst(lds_addr(smem));      // LDS byte address of stage 0
@@ -875,6 +939,148 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Stream-K pieces (kEpiStream).  Every piece stores its accumulators as an
+  // FP32 partial tile -- 16-byte chunks in lane order, chunk q of thread x at
+  // (q * THREADS + x) * 16 -- in a slot of this workgroup: a piece that ends
+  // its tile (the owner, always a workgroup's last piece) in slot `slot` of
+  // the second half of the partial area, which only this workgroup reads
+  // back (after its tile loop, sk_reduce); any other piece in slot `slot` of
+  // the first half, whose flag it then raises for the tile's owner.  Those
+  // partials and the flags take agent-scope (sc1) accesses, which bypass the
+  // non-coherent caches between the XCDs, and a flag is raised only after
+  // the workgroup's partial stores have completed (vmcnt 0 in every wave,
+  // then the barrier).  A flag holds the call's tag in its low word and the
+  // tag's complement in its high word, so that left-over workspace contents
+  // are not taken for it.
+  typedef uint32_t sk_v4u __attribute__((ext_vector_type(4)));
+  constexpr int kSc0 = 1, kSc1 = 16;                // cache policies: L1 bypass, agent scope
+  constexpr uint32_t kSkSlot = (uint32_t)BM * BN * 4;
+  auto sk_flag = [&]() { return ((uint64_t)(~p.sk_tag) << 32) | p.sk_tag; };
+  auto sk_handoff = [&](const Tile& pc) -> bool {
+    if constexpr (SKM) {
+      static_assert(FI * FJ * 4 * C::THREADS * 16 == BM * BN * 4, "a partial slot holds one tile");
+      const bool owner = pc.sk1 == upt;
+      float* base = p.partial + ((owner ? (int64_t)stride : 0) + slot) * (int64_t)(BM * BN);
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)kSkSlot, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t off = (uint32_t)((((i * FJ + j) * 4 + b) * C::THREADS + tid) * 16);
+            const sk_v4u o = sk_v4u{__float_as_uint(acc[i][j][4 * b]), __float_as_uint(acc[i][j][4 * b + 1]),
+                                    __float_as_uint(acc[i][j][4 * b + 2]), __float_as_uint(acc[i][j][4 * b + 3])};
+            if (owner) __builtin_amdgcn_raw_buffer_store_b128(o, prs, (int)off, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b128(o, prs, (int)off, 0, kSc1);
+          }
+      if (!owner) {
+        wait_vm<0>();
+        bar();
+        if (tid == 0) __hip_atomic_store(p.sk_flags + slot, sk_flag(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return true;
+    }
+    return false;
+  };
+  // The owner's reduction, after its tile loop (a workgroup ends at most one
+  // tile: its run is shorter than a tile): waits for the flags of the
+  // workgroups that ran the tile's earlier units, if any (a wait that outlasts
+  // kSkSpin polls -- workgroups not all resident, which the launcher never
+  // makes -- gives up and sets the timeout word: the tile is then wrong, not
+  // hung), adds their partials in K order and then its own, applies bias /
+  // alpha, rounds once and stores 4 columns per chunk; then clears the flags.
+  auto sk_reduce = [&]() {
+    if constexpr (SKM) {
+      int64_t u0, u1;
+      sk_run(u0, u1);
+      const Piece pc = piece(u1 > u0 && (u1 - 1) / upt > u0 / upt ? 1 : 0);
+      if (pc.t >= total || pc.b != upt) return;
+      const Tile tt_ = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, pc.t, kunit, TCOLS, pc.a, pc.b);
+      const int64_t tot = (int64_t)total * upt;
+      const int64_t ut = u0 - pc.a;                      // the tile's first unit
+      const int c_first = (int)(((ut + 1) * stride + tot - 1) / tot) - 1;
+      wait_vm<0>();                                      // this workgroup's own partial
+      if (tid == 0) {
+        for (int c = c_first; c < slot; ++c) {
+          int n = 0;
+          while (__hip_atomic_load(p.sk_flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != sk_flag()) {
+            if (++n >= kSkSpin) {
+              __hip_atomic_store(p.sk_flags + kSkMaxGrid, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+      }
+      bar();
+      asm volatile("" ::: "memory");                     // the partial loads stay behind the wait
+      const __amdgpu_buffer_rsrc_t own = __builtin_amdgcn_make_buffer_rsrc(
+          p.partial + ((int64_t)stride + slot) * (int64_t)(BM * BN), (short)0, (int)kSkSlot, 0x00020000);
+      const uint8_t* obase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.out + tt_.row0 * p.n));
+      const uint32_t obytes = ufirst((uint32_t)((tt_.row_end - tt_.row0) * p.n * 2));
+      const __amdgpu_buffer_rsrc_t orsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(obase), (short)0, (int)obytes, 0x00020000);
+      const uint16_t* bias = p.bias ? p.bias + (int64_t)tt_.g * p.n : nullptr;
+      const float alpha = FMT == kNV ? p.alpha[tt_.g] : 1.0f;
+      const bool f16o = p.out_f16 != 0;
+      constexpr int kQ = FI * FJ * 4, kBatch = 8;
+      for (int q0 = 0; q0 < kQ; q0 += kBatch) {
+        float f[kBatch][4];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) f[e][r] = 0.f;
+        for (int c = c_first; c < slot; ++c) {
+          const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+              p.partial + (int64_t)c * (BM * BN), (short)0, (int)kSkSlot, 0x00020000);
+          sk_v4u v[kBatch];
+#pragma unroll
+          for (int e = 0; e < kBatch; ++e)
+            v[e] = __builtin_bit_cast(sk_v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  prs, (int)(((q0 + e) * C::THREADS + tid) * 16), 0, kSc1));
+#pragma unroll
+          for (int e = 0; e < kBatch; ++e)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[e][r] += __uint_as_float(v[e][r]);
+        }
+        sk_v4u w[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e)
+          w[e] = __builtin_bit_cast(sk_v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                                own, (int)(((q0 + e) * C::THREADS + tid) * 16), 0, kSc0));
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          // chunk q = (i FJ + j) 4 + b: fragment (i, j), columns 8 b + 4 h .. + 3
+          const int q = q0 + e, i = q / (FJ * 4), j = (q / 4) % FJ, b = q % 4;
+          const int64_t mr = wm * WTM + i * 32 + r32;
+          const int64_t n = tt_.n0 + wn * WTN + j * 32 + 8 * b + 4 * h;
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = f[e][r] + __uint_as_float(w[e][r]);
+          if (bias != nullptr && n < p.n) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+            x[0] += bf16_lo(bb.x);
+            x[1] += bf16_hi(bb.x);
+            x[2] += bf16_lo(bb.y);
+            x[3] += bf16_hi(bb.y);
+          }
+          if (FMT == kNV)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] *= alpha;
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          const v2u o = f16o ? v2u{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])}
+                             : v2u{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          const uint32_t off = n < p.n ? (uint32_t)((mr * p.n + n) * 2) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b64(o, orsrc, (int)off, 0, 0);
+        }
+      }
+      if (tid == 0)
+        for (int c = c_first; c < slot; ++c)
+          __hip_atomic_store(p.sk_flags + c, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   bool prior_stores = false;
   while (true) {
@@ -913,11 +1119,18 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
       st ^= 1;
     }
     // last step: the next tile's step 0 goes into the other stage
-    const int t_next = tile_of(round + 1);
+    // (stream-K: the second piece after the first, read from LDS, whose
+    // store the first piece's barriers have long ordered)
+    const Piece pn = !SKM ? Piece{tile_of(round + 1), 0, 0}
+                          : (round == 0 ? Piece{__builtin_amdgcn_readfirstlane(sk_second[0]),
+                                                __builtin_amdgcn_readfirstlane(sk_second[1]),
+                                                __builtin_amdgcn_readfirstlane(sk_second[2])}
+                                        : Piece{total, 0, 0});
+    const int t_next = pn.t;
     const bool has_next = t_next < tile_end;
     Tile tn = tl;
     if (has_next) {
-      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, L::SPG, TCOLS);
+      tn = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, t_next, kunit, TCOLS, pn.a, pn.b);
       // the scale buffer after this tile's last scale group
       tn.sg = (tl.sg + tl.nk / L::SPG) & 1;
       issue<FMT, GS, PAIRED, kSch, NTB>(tn, lo, 0, smem_lds + (st ^ 1) * L::STAGE, smem_lds, w);
@@ -1234,6 +1447,8 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    } else if (sk_handoff(tl)) {
+      // a stream-K piece that does not end its tile: its partial is handed off
     } else {
       // ---- epilogue: BF16 (+bias), 16-byte buffer stores relative to the
       // tile's first row.  32x32 result: lane l holds D[8b + 4(l/32) + r][l%32]
@@ -1312,6 +1527,7 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
     st ^= 1;
     prior_stores = true;
   }
+  sk_reduce();
 }
 
 // Sums the K-split partial tiles slice by slice, in slice order, and writes
@@ -1371,8 +1587,15 @@ int plan_cus(const GemmArgs& p, const DeviceInfo& dev) {
 //    long next to writing and summing its S partial planes: at least about
 //    110 us of matrix work per tail tile on a loaded chip, i.e. 40 FP4 steps,
 //    48 FP8 steps or 12 NVFP4 steps (whose FP16 products are slower).
+//  * Stream-K (dense form) where the tiles make one round of more than a
+//    third of the grid: the K units (of at least two steps, on scale-group
+//    boundaries) of all tiles are dealt out in equal runs, one per
+//    workgroup, when the longest run is at most 0.7 of a tile's units and
+//    saves enough matrix time to pay for the FP32 hand-off (below).
 //  * K split (dense and batch forms) where the tiles cannot fill half of the
-//    CUs: S slices of at least 4 K steps each, S * tiles <= CUs, at most 8.
+//    CUs: S slices of at least 4 K steps each, S * tiles <= CUs, at most 8,
+//    when the steps saved pay for the partial planes (below).
+// Every plan's FP32 partials follow the kWsHeader bytes of stream-K flags.
 SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
   SplitPlan sp{};
   sp.kind = kSplitNone;
@@ -1398,24 +1621,65 @@ SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
       sp.r0 = last_blk * kMB * BM;
       sp.c0 = (NT - cols) * BN;
       sp.rect_tiles = cols * mb;
-      sp.bytes = (uint64_t)(S * (p.m_rows - sp.r0) * (p.n - sp.c0) * 4);
+      sp.bytes = kWsHeader + (uint64_t)(S * (p.m_rows - sp.r0) * (p.n - sp.c0) * 4);
     }
     return sp;
+  }
+  // matrix time of one K step of a 256x256 tile on one CU, in us (dense
+  // 4096 x 17408 x 5120 runs: MXFP8 2.0, MXFP4 2.6, NVFP4 on the FP16 matrix
+  // cores 7.6)
+  const double step_us = p.mode == kMXFP8 ? 2.0 : (p.mode == kMXFP4 ? 2.6 : 7.6);
+  if (p.num_groups == 1 && tiles <= grid_full && tiles * 3 > grid_full && grid_full <= kSkMaxGrid) {
+    // stream-K: K units of at least two steps, on scale-group boundaries.
+    // Each workgroup then moves about 1 MB of FP32 partial tiles (stores and
+    // loads of up to two slots of its own and of the tile's other pieces),
+    // which measured 30 us over 256 workgroups whatever the format: taken
+    // where the steps saved on the longest run are worth 40 us or more
+    // (NVFP4 512 x 17408 x 5120: 141 -> 119 us; MXFP4 at the same shape
+    // saves 8 steps, 21 us, and ran 42 -> 57 us).
+    const bool gs = p.mode == kNVFP4 || p.ldsf % 16 == 0;
+    const int64_t spg = !gs ? 1 : (p.mode == kMXFP8 ? 4 : (p.mode == kMXFP4 ? 2 : 1));
+    const int64_t unit = spg < 2 ? 2 : spg;
+    const int64_t upt = nk / unit;
+    const int64_t run = (tiles * upt + grid_full - 1) / grid_full;   // units of the longest run
+    const double saved_us = (double)(nk - run * unit) * step_us;
+    if (nk % unit == 0 && upt >= 4 && run * 10 <= upt * 7 && saved_us >= 40.0) {
+      sp.kind = kSplitStream;
+      sp.grid = grid_full;
+      sp.upt = (int32_t)upt;
+      sp.unit = (int32_t)unit;
+      sp.bytes = kWsHeader + 2 * (uint64_t)grid_full * BM * BN * 4;   // two partial slots per workgroup
+      return sp;
+    }
   }
   if (tiles * 2 <= cus && nk >= 8) {
     int64_t S = cus / tiles;
     if (S > nk / 4) S = nk / 4;
     if (S > 8) S = 8;
-    if (S >= 2) {
+    // taken where the steps saved outweigh 1.5 times the partial planes'
+    // HBM traffic (S planes written and read, the output written, at 5 TB/s):
+    // MXFP4 512 x 12288 x 5120 (96 tiles, S = 2) saves 10 steps, 26 us,
+    // against 23 us of traffic, and ran 40 us unsplit against 43 us split
+    const double saved_us = (double)(nk - (nk + S - 1) / S) * step_us;
+    const double traffic_us = (double)(S * 8 + 2) * (double)(p.m_rows * p.n) / 5.0e6;
+    if (S >= 2 && saved_us >= 1.5 * traffic_us) {
       sp.kind = kSplitAll;
       sp.S = S;
-      sp.bytes = (uint64_t)(S * p.m_rows * p.n * 4);
+      sp.bytes = kWsHeader + (uint64_t)(S * p.m_rows * p.n * 4);
     }
   }
   return sp;
 }
 
 namespace {
+
+// The flag value of a stream-K call (its low word; a counter, so that calls
+// in a row differ).  The flags are zero again when a call ends; a graph
+// replay repeats its captured tag, which stays correct for that reason.
+uint32_t next_sk_tag() {
+  static std::atomic<uint32_t> tag{0x51u};
+  return tag.fetch_add(1, std::memory_order_relaxed);
+}
 
 template <int FMT, bool GS>
 hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& dev) {
@@ -1429,7 +1693,8 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
                          (const void*)mx_gemm_tiled<FMT, kEpiSplit, GS>,
                          (const void*)mx_gemm_tiled<FMT, kEpiBf16, GS, true>,
                          (const void*)mx_gemm_tiled<FMT, kEpiF16, GS, true>,
-                         (const void*)mx_gemm_tiled<FMT, kEpiSplit, GS, true>};
+                         (const void*)mx_gemm_tiled<FMT, kEpiSplit, GS, true>,
+                         (const void*)mx_gemm_tiled<FMT, kEpiStream, GS>};
     for (const void* fn : fns) {
       const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
       if (e != hipSuccess) return e;
@@ -1463,6 +1728,21 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   // the split, if the plan has one and the caller's workspace holds it
   const SplitPlan sp = plan_split(p, dev);
   const bool split = sp.kind != kSplitNone && p.workspace != nullptr && p.workspace_bytes >= sp.bytes;
+  float* const partial = split ? reinterpret_cast<float*>(static_cast<uint8_t*>(p.workspace) + kWsHeader) : nullptr;
+
+  if (split && sp.kind == kSplitStream) {
+    GemmArgs q = p;
+    q.ksplit = 1;
+    q.tile_limit = 0;
+    q.partial = partial;
+    q.sk_flags = static_cast<uint64_t*>(p.workspace);
+    q.sk_upt = sp.upt;
+    q.sk_unit = sp.unit;
+    q.sk_tag = next_sk_tag();
+    hipLaunchKernelGGL((mx_gemm_tiled<FMT, kEpiStream, GS>), dim3((unsigned)sp.grid), dim3(Cfg<FMT>::THREADS), smem,
+                       s, q);
+    return hipGetLastError();
+  }
 
   if (split && sp.kind == kSplitTail) {
     // The last round's tiles -- a rectangle of whole n-tile columns of the
@@ -1483,7 +1763,7 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
     q2.ldo = p.n;
     q2.ksplit = (int32_t)sp.S;
     q2.tile_limit = 0;
-    q2.partial = static_cast<float*>(p.workspace);
+    q2.partial = partial;
     GemmArgs q1 = p;
     q1.ksplit = 1;
     q1.partial = nullptr;
@@ -1513,7 +1793,7 @@ hipError_t launch_tiled_cfg(hipStream_t s, const GemmArgs& p, const DeviceInfo& 
   q.partial = nullptr;
   if (split && sp.kind == kSplitAll) {
     q.ksplit = (int32_t)sp.S;
-    q.partial = static_cast<float*>(p.workspace);
+    q.partial = partial;
   }
   int64_t grid = cus;
   if (tiles * q.ksplit < grid) grid = tiles * q.ksplit;

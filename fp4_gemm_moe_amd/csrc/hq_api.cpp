@@ -252,7 +252,11 @@ hq_status hq_dense_gemm_scratch(void* stream, int32_t mode, const uint8_t* a, co
   p.num_groups = 1;
   p.m_rows = m;
   p.slot_rows = m;
-  const uint64_t need = hq::gemm_workspace_bytes(p, dev);
+  bool stream_k = false;
+  uint64_t need = hq::gemm_workspace_bytes(p, dev, &stream_k);
+  // a stream-K plan that does not fit the scratch is not taken: the call
+  // runs unsplit, as hq_dense_gemm_ws does with a workspace of that size
+  if (stream_k && need > (uint64_t)HQ_SCRATCH_BYTES) need = 0;
   if (need > (uint64_t)HQ_SCRATCH_BYTES)
     return fail(HQ_ERR_SHAPE, "%s: this shape's K split needs %llu bytes of workspace, more than the %llu "
                 "of the library's scratch (use hq_dense_gemm_ws with a workspace of that size, or hq_dense_gemm)",

@@ -78,13 +78,28 @@ struct GemmArgs {
   const float* prob;
   float* dprob;
   uint16_t* d_out;
+  // Stream-K form of a dense call (tiled kernel, set by the launcher): the
+  // K steps of all tiles form sk_upt units of sk_unit steps per tile, dealt
+  // out in equal runs to the workgroups.  sk_flags: one 64-bit flag per
+  // workgroup at the start of the workspace; sk_tag: this call's flag value.
+  int32_t sk_upt;
+  int32_t sk_unit;
+  uint32_t sk_tag;
+  uint64_t* sk_flags;
 };
+
+// Bytes at the start of a split workspace that hold the stream-K flags (one
+// 64-bit word per workgroup, the last one the spin-timeout word); the FP32
+// partial tiles of every split form follow them.
+constexpr uint64_t kWsHeader = 16384;
+constexpr int kSkMaxGrid = 1023;
 
 // How a dense or batch call on the tiled kernel splits K (plan_split).
 enum SplitKind : int32_t {
   kSplitNone = 0,
   kSplitAll = 1,    // every tile's K steps in S slices
   kSplitTail = 2,   // the last round's tiles (a rectangle at r0, c0) in S slices
+  kSplitStream = 3, // stream-K: equal runs of every tile's K units per workgroup
 };
 struct SplitPlan {
   int32_t kind;
@@ -92,6 +107,8 @@ struct SplitPlan {
   uint64_t bytes;        // FP32 workspace the split needs
   int64_t r0, c0;        // kSplitTail: the rectangle's first row and column
   int64_t rect_tiles;    // kSplitTail: its tiles
+  int64_t grid;          // kSplitStream: workgroups
+  int32_t upt, unit;     // kSplitStream: K units per tile, K steps per unit
 };
 
 struct DeviceInfo {
@@ -113,7 +130,8 @@ hipError_t launch_gemm(hipStream_t s, const GemmArgs& args, const DeviceInfo& de
 // call of this shape uses (0 when it never splits: other forms, the direct
 // kernel).
 SplitPlan plan_split(const GemmArgs& args, const DeviceInfo& dev);
-uint64_t gemm_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev);
+// *stream_k (optional): whether that plan is the stream-K one.
+uint64_t gemm_workspace_bytes(const GemmArgs& args, const DeviceInfo& dev, bool* stream_k = nullptr);
 // The gate|up GEMM with the SwiGLU + re-quant epilogue (args.h > 0); false
 // when the tiled kernel cannot take the shape (K, alignment).
 bool gemm_swiglu_supported(const GemmArgs& args);

@@ -135,22 +135,35 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
  * page's large-M tier: the workspace is allocated by the caller, before any
  * graph capture, and passed on every call).  hq_gemm_workspace_size gives
  * the bytes this shape uses; when workspace_bytes holds them the call may
- * split K:
+ * split K.  The first 16 KB of the workspace hold 64-bit flag words of the
+ * stream-K form; the FP32 partials of every form follow them.
  *  - when the output tiles cannot fill half of the compute units and K is
  *    long (at least 8 K steps of 128 bytes per row), K is cut into 2..8
  *    contiguous slices: each slice's FP32 partial products go to the
  *    workspace (slices * m * n floats), a second kernel adds the slices in
- *    order and applies bias / alpha, then rounds once to BF16;
+ *    order and applies bias / alpha, then rounds once to BF16.  Taken where
+ *    the matrix time saved outweighs the partial planes' memory traffic;
  *  - when the tiles fill whole rounds of the compute units and leave a last
  *    round at most half full, and K is long (at least 48 MXFP8, 40 MXFP4 or
  *    12 NVFP4 steps), the last round's tiles -- whole 256-column tiles of the
  *    last 1024 rows or fewer -- are computed the same way, after the others,
- *    with slices * rows * columns floats of that rectangle.
+ *    with slices * rows * columns floats of that rectangle;
+ *  - stream-K: when the tiles make one round of more than a third of the
+ *    compute units and the matrix time saved pays for the hand-off (long K,
+ *    or NVFP4), the K steps of all tiles are dealt out in equal runs, one
+ *    per workgroup, and each tile's pieces hand their FP32 partial tiles to
+ *    its last piece, which writes the output (two 256 KB partial tiles per
+ *    workgroup).  Its workgroups wait for each other, so the launch must
+ *    have all of them resident at once: it uses at most cu_limit (or all)
+ *    compute units, one workgroup each, and a wait that still finds no
+ *    partial after about a second (other work holding the compute units)
+ *    gives up and sets the last flag word instead of hanging.
  * With a NULL workspace, or fewer bytes than the shape uses, the call runs
  * unsplit (as hq_dense_gemm).  A split changes the FP32 summation order, not
- * the result's contract.  The workspace is scratch: its contents before and
- * after the call mean nothing, and two calls in flight at once (on two
- * streams) need two workspaces.  It must be 16-byte aligned
+ * the result's contract.  The workspace is scratch: its contents before the
+ * call do not change the result (the stream-K flags carry a value of the
+ * call's own and are cleared by the call), and two calls in flight at once
+ * (on two streams) need two workspaces.  It must be 16-byte aligned
  * (HQ_ERR_NULL for a NULL workspace with workspace_bytes > 0).
  */
 hq_status hq_dense_gemm_ws(void* stream, int32_t mode, const uint8_t* a,
@@ -167,8 +180,10 @@ hq_status hq_dense_gemm_ws(void* stream, int32_t mode, const uint8_t* a,
  * per GPU (a static device array, resolved once per device on first use and
  * held until the process ends); the call allocates nothing.  Same arguments,
  * result and split plan as hq_dense_gemm_ws given a workspace of
- * HQ_SCRATCH_BYTES.  A shape whose plan needs more than HQ_SCRATCH_BYTES
- * (hq_gemm_workspace_size) is refused with HQ_ERR_SHAPE before any launch.
+ * HQ_SCRATCH_BYTES.  A shape whose K-split plan needs more than
+ * HQ_SCRATCH_BYTES (hq_gemm_workspace_size) is refused with HQ_ERR_SHAPE
+ * before any launch; a stream-K plan that does not fit is not taken (the
+ * call runs unsplit).
  * Every call on one GPU uses the same scratch: calls that may overlap on a
  * GPU (several streams, several host threads) race and must be serialised
  * by the caller; a call's scratch contents are meaningless afterwards.

@@ -225,19 +225,20 @@ def test_tail_split_random_with_bias_or_alpha(case):
 
 
 def test_workspace_size_query():
-    """The size query follows the split plan: S slices x rows x columns FP32
-    (K split: the whole output; tail split: the last round's rectangle), 0
-    where the call never splits (many tiles, short K, the direct kernel, the
-    grouped forms' shapes)."""
+    """The size query follows the split plan: 16 KB of stream-K flag words,
+    then S slices x rows x columns FP32 (K split: the whole output; tail
+    split: the last round's rectangle), 0 where the call never splits (many
+    tiles, short K, the direct kernel, the grouped forms' shapes)."""
     U.require_gpu()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hdr = 16384
     # (mxfp8, 300 x 520 x 8576): 2 x 3 = 6 tiles, 67 K steps -> S = min(cus / 6, 16, 8) = 8
-    assert hq.hq_gemm_workspace_size("mxfp8", 300, 520, 8576) == min(cus // 6, 8) * 300 * 520 * 4
+    assert hq.hq_gemm_workspace_size("mxfp8", 300, 520, 8576) == hdr + min(cus // 6, 8) * 300 * 520 * 4
     # tail split of 520 x 1544 x 6144 on 16 CUs: a 2-column x 3-m-tile rectangle, S = 2
-    assert hq.hq_gemm_workspace_size("mxfp8", 520, 1544, 6144, cu_limit=16) == 2 * 520 * (1544 - 1280) * 4
+    assert hq.hq_gemm_workspace_size("mxfp8", 520, 1544, 6144, cu_limit=16) == hdr + 2 * 520 * (1544 - 1280) * 4
     assert hq.hq_gemm_workspace_size("mxfp8", 4096, 4096, 256) == 0         # short K
     assert hq.hq_gemm_workspace_size("mxfp4", 16, 4096, 8192) == 0          # direct kernel
-    assert hq.hq_gemm_workspace_size("mxfp8", 100, 128, 4096, batch=3) == min(cus // 3, 8) * 300 * 128 * 4
+    assert hq.hq_gemm_workspace_size("mxfp8", 100, 128, 4096, batch=3) == hdr + min(cus // 3, 8) * 300 * 128 * 4
     assert hq.hq_gemm_workspace_size("mxfp8", 0, 128, 4096) == 0
     with pytest.raises(hq.HQError):
         hq.hq_gemm_workspace_size("mxfp8", 16, 12, 4096)                       # n % 8

@@ -5,8 +5,10 @@ Every tensor -- inputs, outputs, the K-split workspace, the pointer arrays of
 the discrete-weights call -- is allocated before capture; the captured
 sequence is MXFP8 activation quantisation, NVFP4 quantisation with its amax
 pass, the grouped gate|up GEMM with the SwiGLU + re-quant epilogue, a K-split
-dense GEMM (workspace), a tail-split dense GEMM (workspace, CU limit), the
-discrete-weights grouped GEMM, a K-split batch GEMM (workspace), the masked
+dense GEMM (workspace), a tail-split dense GEMM (workspace, CU limit), a
+stream-K dense GEMM (workspace, CU limit: its flag words are cleared by the
+call itself, so every replay starts from the state the previous one left),
+the discrete-weights grouped GEMM, a K-split batch GEMM (workspace), the masked
 grouped GEMM, the standalone SwiGLU + re-quant and the backward dSwiGLU GEMM
 in both output forms (dprob cleared by a fill kernel inside the graph; its
 FP32 atomic adds have no fixed order, so dprob is compared within 1e-5
@@ -60,6 +62,13 @@ def _setup(dev):
     st["tout"] = torch.empty(m2, n2, dtype=torch.bfloat16, device=dev)
     st["tws"] = hq.gemm_workspace("mxfp8", m2, n2, k2, cu_limit=16, device=dev)
     assert st["tws"] is not None
+    # stream-K: 256 x 2560 x 16384 on 24 CUs (10 tiles, runs of 13-14 of their 32 K units)
+    m3, n3, k3 = 256, 2560, 16384
+    st["sa"], st["ssa"], _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (m3, k3)), dev), "mxfp8")
+    st["sb"], st["ssb"], _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (n3, k3), 0.05), dev), "mxfp8")
+    st["skout"] = torch.empty(m3, n3, dtype=torch.bfloat16, device=dev)
+    st["skws"] = hq.gemm_workspace("mxfp8", m3, n3, k3, cu_limit=24, device=dev)
+    assert st["skws"] is not None
     # discrete weights: per-expert tensors and their address arrays, built now
     st["bs"] = [st["wq"][g].clone() for g in range(E)]
     st["sfbs"] = [st["wsf"][g].clone() for g in range(E)]
@@ -93,8 +102,8 @@ def _setup(dev):
     return st
 
 
-OUTS = ["aq", "asf", "nq", "nsf", "ng", "yq", "ysf", "dout", "tout", "pout", "bout", "mout", "sq", "ssf",
-        "dd", "dq", "dsf"]
+OUTS = ["aq", "asf", "nq", "nsf", "ng", "yq", "ysf", "dout", "tout", "skout", "pout", "bout", "mout", "sq",
+        "ssf", "dd", "dq", "dsf"]
 CLOSE = ["dprob", "dprobq"]
 
 
@@ -106,6 +115,8 @@ def _calls(st):
     hq.hq_dense_gemm("mxfp8", st["da"], st["dsa"], st["db"], st["dsb"], st["dout"], workspace=st["dws"])
     hq.hq_dense_gemm("mxfp8", st["ta"], st["tsa"], st["tb"], st["tsb"], st["tout"], cu_limit=16,
                      workspace=st["tws"])
+    hq.hq_dense_gemm("mxfp8", st["sa"], st["ssa"], st["sb"], st["ssb"], st["skout"], cu_limit=24,
+                     workspace=st["skws"])
     hq.hq_group_contiguous_gemm_ptr_array("mxfp8", st["aq"], st["asf"], st["bp"], st["sp"], st["ge"],
                                           st["pout"], n=st["pout"].shape[1])
     hq.hq_batch_gemm("mxfp8", st["ba"], st["bsa"], st["bb"], st["bsb"], st["bout"], workspace=st["bws"])
