@@ -20,8 +20,9 @@ other workload ("configs" in the JSON line; --no-configs skips them, --only
 ID runs one of them alone, e.g. under a profiler):
   d0  dense MXFP8 256^3 (seed 0)
   d1  batch MXFP8 4 x 256^3 with and without bias; dense MXFP4 32 x 512 x 256
-  d2  dense MXFP4 / NVFP4, N = 17408, K = 5120, M in {1, 512, 4096} (caller
-      workspace: K split at M = 512, tail split at 4096)
+  d2  dense MXFP4 / NVFP4, N = 17408, K = 5120, M in {1, 512, 4096} (with the
+      caller workspace the plan asks for: NVFP4 takes stream-K at M = 512 and
+      the tail split at 4096; the MXFP4 cells run unsplit)
   d4  grouped-masked MXFP4, 64 experts x 256-row slots, K = 7168, N = 4096
   n3  the backward grouped GEMM with the dSwiGLU epilogue, MXFP8, the MoE shape
       (32 experts, 65536 routed rows, K = 4096, N = 1536, C / D [rows, 3072]);
