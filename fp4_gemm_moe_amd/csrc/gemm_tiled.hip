@@ -599,30 +599,48 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   const int xi = (int)(blockIdx.x % nxcd), ci = (int)(blockIdx.x / nxcd);
   const int lo_x = (int)((int64_t)total * xi / nxcd);
   const int tile_end = xmajor ? (int)((int64_t)total * (xi + 1) / nxcd) : total;
-  // Stream-K: the tiles' K steps, in tile order, are total * upt units of
-  // p.sk_unit steps; workgroup `slot` takes the units [u0, u1), at most one
-  // tile's worth (the launcher keeps total <= stride), so at most two pieces:
-  // the start of tile (u1 - 1) / upt first, then the end of tile u0 / upt.
-  // Consecutive slots share an XCD, so the pieces of a tile and of its
-  // neighbours in the tile order (which share B columns) meet in one L2.
-  // The pieces are recomputed where they are needed, from an opaque copy of
-  // the slot, so that none of it stays in registers through the K loop.
+  // Stream-K: workgroup b belongs to group x = b % nxcd (the XCD that the
+  // round-robin dispatch gives it) at index l = b / nxcd of the group's
+  // per_xcd workgroups; group x takes the tiles [total x / nxcd,
+  // total (x + 1) / nxcd), whose K steps, in tile order, are units of
+  // p.sk_unit steps, upt per tile, dealt out in equal runs [u0, u1) to its
+  // workgroups -- at most one tile's worth each (the launcher keeps a group's
+  // tiles at most its workgroups), so at most two pieces: the start of tile
+  // (u1 - 1) / upt first, then the end of tile u0 / upt.  A tile's pieces
+  // thus sit in one group, and the pieces before its last one in workgroups
+  // of lower index: dispatched earlier, and never waiting before they hand
+  // their partial on, so every wait for them ends even when the workgroups
+  // are not all resident at once.  The group's tiles are neighbours in the
+  // tile order (sharing B columns) and meet in one L2.  The pieces are
+  // recomputed where they are needed, from an opaque copy of the workgroup
+  // index, so that none of it stays in registers through the K loop.
   const int upt = SKM ? p.sk_upt : 1;
   struct Piece {
     int t, a, b;   // tile, K units [a, b) of its upt
   };
-  auto sk_run = [&](int64_t& u0, int64_t& u1) {
-    int sl = slot;
-    asm volatile("" : "+s"(sl));
-    const int64_t tot = (int64_t)total * upt;
-    u0 = (int64_t)sl * tot / stride;
-    u1 = (int64_t)(sl + 1) * tot / stride;
+  struct SkRun {
+    int64_t u0, u1;      // this workgroup's units (global numbering)
+    int64_t g0, gu;      // the group's first unit and its unit count
+    int base;            // slot of the group's first workgroup
+  };
+  auto sk_run = [&]() -> SkRun {
+    int b = (int)blockIdx.x;
+    asm volatile("" : "+s"(b));
+    const int x = b % nxcd, l = b / nxcd;
+    const int64_t t0 = (int64_t)total * x / nxcd, t1 = (int64_t)total * (x + 1) / nxcd;
+    SkRun r;
+    r.g0 = t0 * upt;
+    r.gu = (t1 - t0) * upt;
+    r.u0 = r.g0 + (int64_t)l * r.gu / per_xcd;
+    r.u1 = r.g0 + (int64_t)(l + 1) * r.gu / per_xcd;
+    r.base = x * per_xcd;
+    return r;
   };
   auto piece = [&](int round) -> Piece {
     Piece pc{total, 0, 0};
     if constexpr (SKM) {
-      int64_t u0, u1;
-      sk_run(u0, u1);
+      const SkRun rn = sk_run();
+      const int64_t u0 = rn.u0, u1 = rn.u1;
       if (u1 > u0 && u1 - u0 <= upt) {
         const int tlo = (int)(u0 / upt), thi = (int)((u1 - 1) / upt);
         if (round == 0) pc = thi > tlo ? Piece{thi, 0, (int)(u1 - (int64_t)thi * upt)}
@@ -986,21 +1004,21 @@ __global__ __launch_bounds__(Cfg<FMT>::THREADS, 1) void mx_gemm_tiled(GemmArgs p
   };
   // The owner's reduction, after its tile loop (a workgroup ends at most one
   // tile: its run is shorter than a tile): waits for the flags of the
-  // workgroups that ran the tile's earlier units, if any (a wait that outlasts
-  // kSkSpin polls -- workgroups not all resident, which the launcher never
-  // makes -- gives up and sets the timeout word: the tile is then wrong, not
-  // hung), adds their partials in K order and then its own, applies bias /
-  // alpha, rounds once and stores 4 columns per chunk; then clears the flags.
+  // workgroups of its group that ran the tile's earlier units, if any (lower
+  // indices: those waits end; a wait that still outlasts kSkSpin polls gives
+  // up and sets the timeout word, so that a fault elsewhere leaves a wrong
+  // tile, not a hung GPU), adds their partials in K order and then its own,
+  // applies bias / alpha, rounds once and stores 4 columns per chunk; then
+  // clears the flags.
   auto sk_reduce = [&]() {
     if constexpr (SKM) {
-      int64_t u0, u1;
-      sk_run(u0, u1);
-      const Piece pc = piece(u1 > u0 && (u1 - 1) / upt > u0 / upt ? 1 : 0);
+      const SkRun rn = sk_run();
+      const Piece pc = piece(rn.u1 > rn.u0 && (rn.u1 - 1) / upt > rn.u0 / upt ? 1 : 0);
       if (pc.t >= total || pc.b != upt) return;
       const Tile tt_ = make_tile<FMT>(p, tt, total_gm, n_heavy, NT, mt_per, nk, pc.t, kunit, TCOLS, pc.a, pc.b);
-      const int64_t tot = (int64_t)total * upt;
-      const int64_t ut = u0 - pc.a;                      // the tile's first unit
-      const int c_first = (int)(((ut + 1) * stride + tot - 1) / tot) - 1;
+      // the slot of the group's workgroup that holds the tile's first unit
+      const int64_t ut = rn.u0 - pc.a - rn.g0;
+      const int c_first = rn.base + (int)(((ut + 1) * per_xcd + rn.gu - 1) / rn.gu) - 1;
       wait_vm<0>();                                      // this workgroup's own partial
       if (tid == 0) {
         for (int c = c_first; c < slot; ++c) {
@@ -1641,7 +1659,11 @@ SplitPlan plan_split(const GemmArgs& p, const DeviceInfo& dev) {
     const int64_t spg = !gs ? 1 : (p.mode == kMXFP8 ? 4 : (p.mode == kMXFP4 ? 2 : 1));
     const int64_t unit = spg < 2 ? 2 : spg;
     const int64_t upt = nk / unit;
-    const int64_t run = (tiles * upt + grid_full - 1) / grid_full;   // units of the longest run
+    // the kernel's groups: grid_full / nx workgroups and at most
+    // ceil(tiles / nx) tiles each (nx = 8 XCDs, or 1 below 8 CUs)
+    const int64_t nx = grid_full >= 8 ? 8 : 1, per = grid_full / nx;
+    const int64_t tpg = (tiles + nx - 1) / nx;
+    const int64_t run = (tpg * upt + per - 1) / per;                   // units of the longest run
     const double saved_us = (double)(nk - run * unit) * step_us;
     if (nk % unit == 0 && upt >= 4 && run * 10 <= upt * 7 && saved_us >= 40.0) {
       sp.kind = kSplitStream;

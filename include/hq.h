@@ -151,13 +151,17 @@ hq_status hq_dense_gemm(void* stream, int32_t mode, const uint8_t* a,
  *  - stream-K: when the tiles make one round of more than a third of the
  *    compute units and the matrix time saved pays for the hand-off (long K,
  *    or NVFP4), the K steps of all tiles are dealt out in equal runs, one
- *    per workgroup, and each tile's pieces hand their FP32 partial tiles to
- *    its last piece, which writes the output (two 256 KB partial tiles per
- *    workgroup).  Its workgroups wait for each other, so the launch must
- *    have all of them resident at once: it uses at most cu_limit (or all)
- *    compute units, one workgroup each, and a wait that still finds no
- *    partial after about a second (other work holding the compute units)
- *    gives up and sets the last flag word instead of hanging.
+ *    per workgroup (in 8 groups -- every eighth workgroup, one XCD's share
+ *    under the round-robin dispatch -- each taking an eighth of the tiles),
+ *    and each tile's pieces hand their FP32 partial tiles to its last
+ *    piece, which writes the output (two 256 KB partial tiles per
+ *    workgroup).  A piece waits only for workgroups of lower index,
+ *    dispatched before it (in index order), which hand their partial on
+ *    before they wait for
+ *    anything, so the waits end whether or not the launch's workgroups are
+ *    all resident at once; a wait that still finds no partial after about a
+ *    second (a fault elsewhere) gives up and sets the last flag word instead
+ *    of hanging.
  * With a NULL workspace, or fewer bytes than the shape uses, the call runs
  * unsplit (as hq_dense_gemm).  A split changes the FP32 summation order, not
  * the result's contract.  The workspace is scratch: its contents before the

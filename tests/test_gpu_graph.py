@@ -62,7 +62,8 @@ def _setup(dev):
     st["tout"] = torch.empty(m2, n2, dtype=torch.bfloat16, device=dev)
     st["tws"] = hq.gemm_workspace("mxfp8", m2, n2, k2, cu_limit=16, device=dev)
     assert st["tws"] is not None
-    # stream-K: 256 x 2560 x 16384 on 24 CUs (10 tiles, runs of 13-14 of their 32 K units)
+    # stream-K: 256 x 2560 x 16384 on 24 CUs (10 tiles, 1-2 per group of 3 workgroups, runs of
+    # 10-22 of their 32 K units)
     m3, n3, k3 = 256, 2560, 16384
     st["sa"], st["ssa"], _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (m3, k3)), dev), "mxfp8")
     st["sb"], st["ssb"], _ = hq.quantize(U.dev_bf16(synth.normal_bf16(rng, (n3, k3), 0.05), dev), "mxfp8")

@@ -3,17 +3,19 @@
 A dense launch whose tiles make one round of more than a third of the grid
 (and at most all of it) deals the K units of all tiles out in equal runs, one
 per workgroup, where that saves enough matrix time (long K, or NVFP4's slower
-steps): a tile's pieces then sit in two to four workgroups, which hand their
-FP32 partial tiles to the tile's last piece.  A CU limit sets the grid at
-these sizes:
-  * MXFP8 256 x 2560 x 16384 on 16 CUs: 10 tiles of 32 units of 4 steps,
-    runs of 20 units (each tile in two pieces);
-  * the same on 24 CUs: runs of 13 or 14 units (tiles in three or four
-    pieces, up to three partials per tile);
-  * MXFP4 300 x 1280 x 16384 (a ragged second m-tile; 32 units of 2 steps)
-    and NVFP4 256 x 2552 x 4096 (a partial last n-tile; 8 units of 2 steps)
-    on 16 CUs;
-  * MXFP8 512 x 3072 x 8192 on 40 CUs: 24 tiles of 16 units, runs of 9 or 10.
+steps).  The workgroups form 8 groups (every eighth one), each taking an
+eighth of the tiles; a tile's pieces sit in two or more workgroups of its
+group, which hand their FP32 partial tiles to the tile's last piece.  A CU
+limit sets the grid at these sizes:
+  * MXFP8 256 x 4096 x 6144 on 32 CUs: 16 tiles of 12 units of 4 steps, 2 per
+    group of 4 workgroups, runs of 6 units (each tile in two pieces);
+  * MXFP8 256 x 2816 x 6144 on 32 CUs: 11 tiles, so five groups hold one tile
+    over their 4 workgroups (four pieces, three partials per tile) and three
+    hold two;
+  * MXFP4 300 x 2048 x 16384 (a ragged second m-tile; 32 units of 2 steps)
+    on 32 CUs, and NVFP4 256 x 2552 x 8192 (a partial last n-tile; 16 units of
+    2 steps) on 24 CUs (groups of 3 workgroups: three pieces per tile);
+  * MXFP8 512 x 3072 x 8192 on 40 CUs: 24 tiles of 16 units, 3 per group of 5.
 Integer-coded inputs make every partial sum exact, so the result is
 bit-exact whatever the summation order; random inputs meet the acceptance
 bound against the oracle.  Flag words that start at zero are zero again
@@ -36,8 +38,8 @@ pytestmark = pytest.mark.gpu
 HEADER = 16384            # flag words at the start of a split workspace
 SLOT = 256 * 256 * 4      # one FP32 partial tile
 
-CASES = [("mxfp8", 256, 2560, 16384, 16), ("mxfp8", 256, 2560, 16384, 24), ("mxfp4", 300, 1280, 16384, 16),
-         ("nvfp4", 256, 2552, 4096, 16), ("mxfp8", 512, 3072, 8192, 40)]
+CASES = [("mxfp8", 256, 4096, 6144, 32), ("mxfp8", 256, 2816, 6144, 32), ("mxfp4", 300, 2048, 16384, 32),
+         ("nvfp4", 256, 2552, 8192, 24), ("mxfp8", 512, 3072, 8192, 40)]
 _IDS = [f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-cu{c[4]}" for c in CASES]
 
 
