@@ -136,3 +136,28 @@ def test_stream_k_left_over_workspace_contents():
     assert np.array_equal(_run(mode, a, sfa, b, sfb, m, n, k, dev, cus, ws), ref)
     for _ in range(3):
         assert np.array_equal(_run(mode, a, sfa, b, sfb, m, n, k, dev, cus, ws), ref)
+
+
+def test_stream_k_beside_other_work():
+    """Stream-K calls while FP32 matrix products run on another stream and
+    hold compute units: a piece waits only for workgroups dispatched before
+    it, so the results stay those of the idle GPU and no wait gives up (the
+    spin-timeout word, the last flag word, stays clear)."""
+    dev = U.require_gpu()
+    mode, m, n, k, cus = CASES[1]
+    rng = np.random.default_rng(321)
+    a, sfa, _ = _quant(synth.normal_bf16(rng, (m, k)), mode)
+    b, sfb, _ = _quant(synth.normal_bf16(rng, (n, k), 0.05), mode)
+    ws = hq.gemm_workspace(mode, m, n, k, cu_limit=cus, device=dev)
+    ws[:HEADER].zero_()
+    ref = _run(mode, a, sfa, b, sfb, m, n, k, dev, cus, ws)
+    other = torch.cuda.Stream()
+    x = torch.randn(4096, 4096, device=dev)
+    for _ in range(4):
+        with torch.cuda.stream(other):
+            y = x
+            for _ in range(12):
+                y = torch.mm(y, x) * 1e-2
+        assert np.array_equal(_run(mode, a, sfa, b, sfb, m, n, k, dev, cus, ws), ref)
+    torch.cuda.synchronize()
+    assert _flags_clear(ws) == 0
