@@ -3,10 +3,11 @@ against hq_dense_gemm_ws with a caller workspace, through the C ABI.
 
 Two calls in a row (the second with a smaller input) must each give the same
 bits as hq_dense_gemm_ws with a workspace of the plan's size (same split plan,
-same kernels), and both are within the acceptance bound of the oracle.  A
-shape whose split needs more than the library's scratch is refused before any
-launch (its output untouched); a shape that does not split runs as
-hq_dense_gemm.
+same kernels), and both are within the acceptance bound of the oracle (the
+calls include a stream-K plan that fits the scratch).  A shape whose K split
+needs more than the library's scratch is refused before any launch (its
+output untouched); a stream-K plan that needs more is not taken (the call
+runs unsplit); a shape that does not split runs as hq_dense_gemm.
 """
 import numpy as np
 import pytest
@@ -58,8 +59,11 @@ def _run(fn, mode, ops, m, n, dev, cu_limit=0):
     return U.host_bits(out)
 
 
-# (mode, m, n, k, cu_limit): a K split of every tile, a smaller one, a tail split
-CASES = [("mxfp8", 300, 520, 8576, 0), ("mxfp4", 200, 264, 8448, 0), ("mxfp8", 520, 1544, 6144, 16)]
+# (mode, m, n, k, cu_limit): a K split of every tile, a smaller one, a tail split, a
+# stream-K plan that fits the scratch (16 tiles over 32 workgroups: 16.4 MB of flags and
+# partial slots, the flags at the scratch's start zero from load and after every call)
+CASES = [("mxfp8", 300, 520, 8576, 0), ("mxfp4", 200, 264, 8448, 0), ("mxfp8", 520, 1544, 6144, 16),
+         ("mxfp8", 256, 4096, 6144, 32)]
 
 
 def test_scratch_equals_workspace_call_twice_in_a_row():
@@ -107,3 +111,32 @@ def test_scratch_without_split_equals_plain_call():
                      bias=U.dev_bf16(bias, dev))
     torch.cuda.synchronize()
     assert np.array_equal(got, U.host_bits(out))
+
+
+def test_scratch_runs_a_larger_stream_k_plan_unsplit():
+    """A stream-K plan that needs more than the scratch is not taken (rather
+    than refused): the call runs unsplit, with the bits of hq_dense_gemm
+    without a workspace."""
+    dev = U.require_gpu()
+    mode, m, n, k = "nvfp4", 512, 17408, 5120
+    need = hq.hq_gemm_workspace_size(mode, m, n, k)
+    if need <= hq.HQ_SCRATCH_BYTES:
+        pytest.skip(f"this device's split plan for the shape needs {need} bytes: fits")
+    U.banner(f"no-alloc dense gemm runs {mode} {m}x{n}x{k} unsplit ({need} bytes planned)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=g)
+    sa = torch.randint(0x30, 0x40, (m, k // 16), dtype=torch.uint8, device=dev, generator=g)
+    sb = torch.randint(0x30, 0x40, (n, k // 16), dtype=torch.uint8, device=dev, generator=g)
+    alpha = torch.ones(1, dtype=torch.float32, device=dev)
+    outs = []
+    for fn in ("scratch", "plain"):
+        out = torch.full((m, n), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        if fn == "scratch":
+            hq.hq_dense_gemm_scratch(mode, a, sa, b, sb, out, alpha=alpha)
+        else:
+            hq.hq_dense_gemm(mode, a, sa, b, sb, out, alpha=alpha)
+        torch.cuda.synchronize()
+        outs.append(U.host_bits(out))
+    assert np.array_equal(outs[0], outs[1])
