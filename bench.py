@@ -33,7 +33,8 @@ ID runs one of them alone, e.g. under a profiler):
 each with its time per launch (HIP events around batches of back-to-back
 launches queued behind a spin kernel, so that short kernels are timed
 without the host's launch latency or per-launch event markers), achieved rate, roofline fraction and, where affordable, the
-oracle's time for the same work on the host cores.
+oracle's time for the same work on the host cores (the d2 cells above M = 1:
+its rate on 8 of the rows).
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
 of the valid rows per second), the per-kernel times, the roofline of the
@@ -673,6 +674,7 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
                 continue
             wq, wsf, gw = hq.quantize(w, mode)
             gs = 16 if mode == "nvfp4" else 32
+            wora = None                         # the oracle's weight codes, quantised once per mode
             for m in (1, 512, 4096):
                 cid = f"d2_{mode}_M{m}"
                 if not want(cid):
@@ -694,15 +696,24 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
                     fns = [lambda: hq.hq_dense_gemm(mode, aq, asf, wq, wsf, out, alpha=alpha, workspace=ws)]
                 med, mean = _launch_us(torch, fns, reps=30 if m < 4096 else 20)
                 extra = {"mean_us": round(mean, 2), "workspace_bytes": 0 if ws is None else ws.numel()}
-                if oracle and m == 1:
+                if oracle:
+                    # M = 1: the whole call; larger M: the oracle's time for 8 of the
+                    # rows (every m/8-th), as a rate (its time grows with the rows)
+                    if wora is None:
+                        wora = Q.nvfp4_quant_bf16(wbits) if mode == "nvfp4" else Q.mx_quant_bf16(wbits, mode) + (None,)
+                    cb, sb_, g_b = wora
+                    rows = np.arange(m) if m == 1 else np.arange(0, m, m // 8)
                     if mode == "nvfp4":
-                        ca, sa_, g_a = Q.nvfp4_quant_bf16(abits)
-                        cb, sb_, g_b = Q.nvfp4_quant_bf16(wbits)
+                        ca, sa_, g_a = Q.nvfp4_quant_bf16(abits[rows])
                         al = np.float32(np.float32(g_a) * np.float32(g_b))
                     else:
-                        (ca, sa_), (cb, sb_), al = Q.mx_quant_bf16(abits, mode), Q.mx_quant_bf16(wbits, mode), None
-                    extra.update(oracle_us=round(_oracle_us(lambda: G.dense_gemm(mode, ca, sa_, cb, sb_, alpha=al),
-                                                            reps=1), 1), oracle_cores=threads)
+                        (ca, sa_), al = Q.mx_quant_bf16(abits[rows], mode), None
+                    ous = _oracle_us(lambda: G.dense_gemm(mode, ca, sa_, cb, sb_, alpha=al), reps=1)
+                    if m == 1:
+                        extra.update(oracle_us=round(ous, 1), oracle_cores=threads)
+                    else:
+                        extra.update(oracle_TFLOP_s=round(2.0 * len(rows) * n * k / (ous * 1e-6) / 1e12, 5),
+                                     oracle_sample=f"{len(rows)} of {m} rows", oracle_cores=threads)
                 if m == 1:
                     emit(_rec(cid, f"dense_{mode}_M{m}_N{n}_K{k}_cold", med, flops=flops, bytes_=bytes_,
                               bound="hbm", **extra))
