@@ -33,8 +33,8 @@ ID runs one of them alone, e.g. under a profiler):
 each with its time per launch (HIP events around batches of back-to-back
 launches queued behind a spin kernel, so that short kernels are timed
 without the host's launch latency or per-launch event markers), achieved rate, roofline fraction and, where affordable, the
-oracle's time for the same work on the host cores (the d2 cells above M = 1:
-its rate on 8 of the rows).
+oracle's time for the same work on the host cores (the d2 cells above M = 1,
+d4 and n3: its rate on a sample of the rows, named in the record).
 
 Output: one JSON line with the whole-step throughput (algorithmic GEMM FLOPs
 of the valid rows per second), the per-kernel times, the roofline of the
@@ -744,9 +744,19 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
                                reps=20)
         experts = int((counts > 0).sum())
         bytes_ = T * K * (0.5 + 1 / 32) + experts * N * K * (0.5 + 1 / 32) + 2 * T * N
+        extra = {}
+        if oracle:
+            # the oracle's rate on the valid rows of the first expert that has any
+            g = int(np.argmax(counts > 0))
+            rows = int(counts[g])
+            ca, sa_ = Q.mx_quant_bf16(d["a"][g * Mmax:g * Mmax + rows], "mxfp4")
+            cb, sb_ = Q.mx_quant_bf16(d["b"][g], "mxfp4")
+            ous = _oracle_us(lambda: G.dense_gemm("mxfp4", ca, sa_, cb, sb_), reps=1)
+            extra = dict(oracle_TFLOP_s=round(2.0 * rows * N * K / (ous * 1e-6) / 1e12, 5),
+                         oracle_sample=f"expert {g}: {rows} of {T} rows", oracle_cores=threads)
         emit(_rec("d4", "moe_grouped_masked_mxfp4_E64_Mmax256_K7168_N4096", med, flops=2.0 * T * N * K,
                   bytes_=bytes_, bound="hbm", mean_us=round(mean, 2), routed_rows=T,
-                  mfma_frac=round(2.0 * T * N * K / (med * 1e-6) / 1e12 / PEAK_TFLOPS["mxfp4"], 4)))
+                  mfma_frac=round(2.0 * T * N * K / (med * 1e-6) / 1e12 / PEAK_TFLOPS["mxfp4"], 4), **extra))
         del aq, asf, wq, wsf, out, d
         torch.cuda.empty_cache()
 
@@ -774,10 +784,24 @@ def run_configs(torch, hq, synth, only=None, oracle=True):
             med, mean = _launch_us(torch, [lambda: hq.hq_group_contiguous_gemm_dswiglu(
                 "mxfp8", qa, sa, qw, sw, ge, c, prob, dprob, dout, alpha=al, beta=be)], reps=20)
             t_ideal = max(flops / (PEAK_TFLOPS["mxfp8"] * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9))
+            extra = {}
+            if oracle:
+                # the oracle's rate on 256 rows of the first non-empty group
+                from oracle import dglu as DG
+                g = int(np.argmax(counts > 0))
+                r0 = int(ends[g - 1]) if g > 0 else 0
+                rows = min(256, int(counts[g]))
+                ca, sa_ = Q.mx_quant_bf16(d["a"][r0:r0 + rows], "mxfp8")
+                cb, sb_ = Q.mx_quant_bf16(d["b"][g], "mxfp8")
+                ous = _oracle_us(lambda: DG.grouped_gemm_dswiglu(
+                    "mxfp8", ca, sa_, cb[None], sb_[None], np.array([rows]), d["c"][r0:r0 + rows],
+                    d["prob"][r0:r0 + rows], alpha=d["alpha"][g:g + 1], beta=d["beta"][g:g + 1]), reps=1)
+                extra = dict(oracle_TFLOP_s=round(2.0 * rows * N * K / (ous * 1e-6) / 1e12, 5),
+                             oracle_sample=f"{rows} rows of group {g}", oracle_cores=threads)
             emit(_rec("n3", "moe_bwd_dswiglu_mxfp8_E32_T65536_K4096_N1536", med, flops=flops, bytes_=bytes_,
                       bound="mfma", mean_us=round(mean, 2), routed_rows=T,
                       hbm_frac=round(bytes_ / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
-                      roofline_frac=round(t_ideal / (med * 1e-6), 3)))
+                      roofline_frac=round(t_ideal / (med * 1e-6), 3), **extra))
         if want("n3_q"):
             # the same with D written row-quantised (MXFP8 codes + UE8M0 per 32)
             dq = torch.empty(R, 2 * N, dtype=torch.uint8, device=dev)
